@@ -1,0 +1,164 @@
+/*
+ * flint_moe.h -- C ABI of the MI355X (gfx950) Flint-style sparse MoE FFN layer.
+ *
+ * The layer (pages about the Flint model: recipes.vllm.ai "RecursiveSI/flint",
+ * section Overview; neoteo.com specification table, row "Eksperci"; news.ditty.ir,
+ * third paragraph):  each token is routed by sigmoid scores to the top 6 of 256 routed
+ * experts, and one shared expert is always active.  Readings where the pages are silent:
+ * router logits are a linear map of the token (fp32 weights, fp32 accumulation), the
+ * selection orders experts by logit (descending) with the lowest index winning ties,
+ * the k sigmoid scores are renormalised to sum to one, every expert is a SwiGLU FFN
+ * down(silu(gate x) * up x), and the shared expert is ungated with weight one.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless stated; all work is queued asynchronously on
+ *     `stream` (a hipStream_t; NULL = the null stream).  No call allocates memory or
+ *     synchronises the host.  The caller owns every buffer.
+ *   - Tensors are row-major and dense.  bf16 values are passed as their uint16 bits.
+ *   - Inputs are never written.  Outputs are fully overwritten (no pre-zeroing needed)
+ *     and must not alias inputs.
+ *   - Every call returns a status (FLINT_OK == 0).  Arguments are validated before any
+ *     HIP call, so invalid arguments are reported without touching the device.
+ *     Nothing throws across the ABI.
+ *   - T == 0 is a no-op returning FLINT_OK once the descriptor is valid.
+ *   - Supported shapes: 1 <= E <= 256; 1 <= k <= min(8, E); n_shared in {0, 1};
+ *     hidden % 64 == 0 and 64 <= hidden <= 8192; inter % 64 == 0 and
+ *     64 <= inter <= 4096; 0 <= T <= 65536.  Every pointer must be 16-byte aligned.
+ *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------ */
+enum {
+    FLINT_OK = 0,
+    FLINT_ERR_NULL = 1,        /* a required pointer is NULL                            */
+    FLINT_ERR_SHAPE = 2,       /* descriptor or T outside the supported range           */
+    FLINT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                      */
+    FLINT_ERR_WORKSPACE = 4,   /* ws_bytes < flint_moe_workspace_bytes(desc, T, format)  */
+    FLINT_ERR_FORMAT = 5,      /* unknown weight format or missing scale arrays         */
+    FLINT_ERR_HIP = 6          /* a kernel launch failed; see flint_moe_status_string    */
+};
+
+/* ---- weight formats ---------------------------------------------------------------- */
+enum {
+    FLINT_WFMT_BF16 = 0,
+    /* NVFP4 run as W4A16 (recipes.vllm.ai "RecursiveSI/flint", Overview: the NVFP4
+       checkpoint is run as W4A16).  Reading of the format: 16 consecutive elements along
+       K share one E4M3FN scale; elements are E2M1 (bit 3 = sign, magnitudes
+       0, .5, 1, 1.5, 2, 3, 4, 6), two per byte, the even column in the low nibble; one
+       fp32 scale per (expert, matrix).  value = e2m1 * e4m3 * tensor_scale. */
+    FLINT_WFMT_NVFP4 = 1
+};
+
+/* ---- route flags ------------------------------------------------------------------- */
+enum {
+    FLINT_ROUTE_LOGITS_IN = 1  /* `logits` is an input; the router product is skipped    */
+};
+
+/* Layer shape.  hidden = H, inter = I (per expert, the shared expert too),
+   n_experts = E routed experts, top_k = k, n_shared = 0 or 1,
+   renormalize = 1: w_j = s_j / sum_i s_i; 0: w_j = s_j (s = sigmoid of the logit). */
+typedef struct {
+    int32_t hidden;
+    int32_t inter;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t n_shared;
+    int32_t renormalize;
+} flint_moe_desc;
+
+/* Expert weights.  Each matrix is stored with K (its input dimension) contiguous:
+   gate and up are [I][H] per expert, down is [H][I] per expert.  Routed experts are
+   stored expert-major; the shared expert has its own pointers (NULL iff n_shared == 0).
+     BF16:  gate, up: uint16 [E][I][H];  down: uint16 [E][H][I].
+     NVFP4: gate, up: uint8 [E][I][H/2]; down: uint8 [E][H][I/2]  (packed E2M1);
+            *_sf: E4M3 block scales, gate/up [E][I][H/16], down [E][H][I/16];
+            gate_ts, up_ts, down_ts: fp32 [E] tensor scales (device memory);
+            sh_ts: fp32 [3] = gate, up, down tensor scales of the shared expert.
+   Scale pointers must be NULL for BF16. */
+typedef struct {
+    int32_t format;
+    const void *gate, *up, *down;
+    const void *sh_gate, *sh_up, *sh_down;
+    const uint8_t *gate_sf, *up_sf, *down_sf;
+    const uint8_t *sh_gate_sf, *sh_up_sf, *sh_down_sf;
+    const float *gate_ts, *up_ts, *down_ts;
+    const float *sh_ts;
+} flint_moe_weights;
+
+/* Optional routing outputs of flint_moe_layer; any member may be NULL. */
+typedef struct {
+    float *logits;          /* [T][E] fp32                                     */
+    int32_t *topk_ids;      /* [T][k]                                           */
+    float *topk_w;          /* [T][k]                                           */
+    int32_t *counts;        /* [E]                                              */
+    int32_t *offsets;       /* [E+1]                                            */
+    int32_t *sorted_assign; /* [T*k]                                            */
+    int32_t *assign_pos;    /* [T*k]                                            */
+} flint_moe_routing;
+
+/* Workspace bytes that route/permute/forward/layer need for any T <= T_max with the
+   given weight format.  Returns 0 for an invalid descriptor or T_max < 0. */
+size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int32_t format);
+
+/* Static text for a status code; for FLINT_ERR_HIP it also names the last HIP error
+   seen by this library (the text is per thread and stays valid until the next call). */
+const char *flint_moe_status_string(int status);
+
+/* Router and selection.
+     logits[t][e] = sum_h x[t][h] * w_router[e][h] + (logit_bias ? logit_bias[e] : 0),
+   accumulated in fp32 (x: bf16 [T][H]; w_router: fp32 [E][H]; logit_bias: fp32 [E]).
+   topk_ids[t][0..k) = the k experts ordered by (logit descending, index ascending) on
+   the fp32 logits, with -0 == +0 and NaN ordered below -inf;
+   topk_w[t][j] = sigmoid(logit) in fp32, divided by the sum over j if desc->renormalize.
+   flags & FLINT_ROUTE_LOGITS_IN: `logits` is read instead (x, w_router may be NULL).
+   Otherwise `logits` may be NULL (kept in the workspace) or receives the logits. */
+int flint_moe_route(const flint_moe_desc *desc, int64_t T, const uint16_t *x,
+                    const float *w_router, const float *logit_bias, float *logits,
+                    int32_t *topk_ids, float *topk_w, uint32_t flags, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/* Grouping of the T*k assignments a = t*k + j by expert id:
+   counts[e] = #assignments of expert e; offsets = exclusive scan (offsets[E] = T*k);
+   sorted_assign = assignments grouped by expert, ascending a inside a group;
+   assign_pos[a] = position of a in sorted_assign.  Integer, bit-exact.
+   Ids outside [0, E) are a caller error: their assignments are dropped. */
+int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk_ids,
+                      int32_t *counts, int32_t *offsets, int32_t *sorted_assign,
+                      int32_t *assign_pos, void *ws, size_t ws_bytes, void *stream);
+
+/* Experts and combine:
+     y[t] = bf16( o_shared(t) + sum_j topk_w[t][j] * o_{topk_ids[t][j]}(t) ),
+     o_e(t) = down_e( silu(gate_e x_t) * (up_e x_t) ),
+   summed in fp32 in that order (shared first, then j ascending), which makes y
+   deterministic.  The expert intermediate h is rounded to bf16 before `down` on the
+   grouped-GEMM path (T > 32), and each per-slot output o is rounded to bf16 there
+   before the combine; the streaming path (T <= 32) keeps both in fp32.
+   topk_ids/topk_w/offsets/sorted_assign/assign_pos are the outputs of route and
+   permute for the same T.  y: bf16 [T][H]. */
+int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
+                      const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                      const int32_t *offsets, const int32_t *sorted_assign,
+                      const int32_t *assign_pos, uint16_t *y, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* The whole layer: route (x, w_router, logit_bias), permute and forward, with the same
+   results as the three calls above.  `routing` (may be NULL) receives the intermediate
+   routing tensors the caller asks for. */
+int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
+                    const uint16_t *x, const float *w_router, const float *logit_bias,
+                    uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,394 @@
+"""Pins of the reference (oracle/) against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: a brute-force
+algorithm, a library routine, a closed form, an invariant or a published codec table.
+No GPU is needed.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from sparse_moe_transformer_wave_amd import datagen as dg
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def bf16_bits(a):
+    return dg.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def bf16_val(bits):
+    return dg.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def make_bf16_experts(n, H, I, std=0.05, seed=0):
+    r = np.random.default_rng(seed)
+    g = bf16_bits(r.normal(0, std, (n, I, H)))
+    u = bf16_bits(r.normal(0, std, (n, I, H)))
+    d = bf16_bits(r.normal(0, std, (n, H, I)))
+    return oracle.Experts(oracle.FMT_BF16, H, I, {"gate": g, "up": u, "down": d})
+
+
+def dense_swiglu(x, g, u, d):
+    """Independent dense SwiGLU in numpy fp64: d @ (silu(g @ x) * (u @ x))."""
+    a = g @ x
+    return d @ (a * scipy.special.expit(a) * (u @ x))
+
+
+# ------------------------------------------------------------------------- codecs
+def test_e2m1_table_matches_ocp_spec():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "e2m1_table.txt")) if not l.startswith("#")]
+    for code, val in rows:
+        v = oracle.e2m1_value(int(code))
+        assert v == float(val) and math.copysign(1, v) == math.copysign(1, float(val))
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if math.isnan(ref[c]):
+            assert math.isnan(v), c
+        else:
+            assert v == ref[c] and math.copysign(1, v) == math.copysign(1, ref[c]), c
+
+
+def test_e4m3_special_values_golden():
+    for line in open(os.path.join(GOLDEN, "e4m3_special.txt")):
+        if line.startswith("#"):
+            continue
+        code, val = line.split()
+        v = oracle.e4m3_value(int(code, 16))
+        if val == "nan":
+            assert math.isnan(v)
+        else:
+            assert v == float(val) and math.copysign(1, v) == math.copysign(1, float(val))
+
+
+def test_e4m3_encode_rne_vs_torch():
+    # every finite code value, every midpoint between neighbours, and random values
+    vals = [oracle.e4m3_value(c) for c in range(0x7F)]
+    mids = [(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])]
+    rnd = list(np.abs(rng.normal(0, 30, 2000))) + list(np.abs(rng.normal(0, 0.01, 2000)))
+    cand = vals + mids + rnd + [v * (1 + 2**-20) for v in mids] + [v * (1 - 2**-20) for v in mids]
+    for v in cand:
+        if v >= 464:  # torch overflows to NaN past the last midpoint; we saturate
+            continue
+        ref = torch.tensor([v], dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8).item()
+        assert oracle.e4m3_encode(v) == ref, v
+    assert oracle.e4m3_encode(1000.0) == 0x7E
+    assert oracle.e4m3_encode(-3.0) == (oracle.e4m3_encode(3.0) | 0x80)
+
+
+def _e2m1_rne_by_binade(v):
+    """Independent E2M1 rounding: scale into the binade, round the mantissa half-even."""
+    m = abs(v)
+    if m >= 6.0:
+        c = 7
+    elif m < 1.0:
+        c = int(round(m * 2))  # Python round(): half to even -> codes 0, 1, 2
+    elif m < 2.0:
+        c = 2 + int(round((m - 1.0) * 2))
+    elif m < 4.0:
+        c = 4 + int(round((m / 2 - 1.0) * 2))
+    else:
+        c = 6 + int(round((m / 4 - 1.0) * 2))
+    return c | (8 if math.copysign(1, v) < 0 else 0)
+
+
+def test_e2m1_encode_rne():
+    grid = [0, .5, 1, 1.5, 2, 3, 4, 6]
+    mids = [(a + b) / 2 for a, b in zip(grid[:-1], grid[1:])]
+    cand = grid + mids + [m + 1e-9 for m in mids] + [m - 1e-9 for m in mids] + \
+        list(rng.uniform(-7, 7, 3000)) + [-0.0, 6.5, 100.0, -100.0]
+    for v in cand:
+        assert oracle.e2m1_encode(v) == _e2m1_rne_by_binade(v), v
+    # ties go to the even code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 5 -> 4
+    assert [oracle.e2m1_value(oracle.e2m1_encode(v)) for v in (0.25, 0.75, 1.25, 5.0)] == [0, 1, 1, 4]
+
+
+E2M1 = np.array([oracle.e2m1_value(c) for c in range(16)])
+E4M3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def dequant_np(q, sb, st):
+    """Independent vectorised dequantisation: table lookups + numpy broadcasting."""
+    N = q.shape[0]
+    codes = np.empty((N, q.shape[1] * 2), np.int64)
+    codes[:, 0::2] = q & 15
+    codes[:, 1::2] = q >> 4
+    return E2M1[codes] * np.repeat(E4M3[sb], 16, axis=1) * st
+
+
+def test_nvfp4_quantiser_roundtrip_on_representable():
+    N, K = 8, 64
+    q = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    q[:, 0] = (q[:, 0] & 0xF0) | 7  # every block ... make column 0 of block 0 a 6.0
+    for b in range(K // 16):
+        q[:, b * 8] = (q[:, b * 8] & 0xF0) | rng.choice([7, 15], N)  # a +-6 in every block
+    sb = rng.integers(0x30, 0x7E, (N, K // 16)).astype(np.uint8)
+    sb[3, 1] = 0x7E  # the largest block scale is 448
+    st = np.float32(0.02 / 2688)
+    W = dequant_np(q, sb, float(st))
+    q2, sb2, st2 = oracle.nvfp4_quantize(W)
+    assert st2 == float(st)
+    np.testing.assert_array_equal(sb2, sb)
+    np.testing.assert_array_equal(dequant_np(q2, sb2, st2), W)
+
+
+def test_nvfp4_quantiser_error_bound():
+    W = rng.normal(0, 0.02, (16, 256))
+    q, sb, st = oracle.nvfp4_quantize(W)
+    D = dequant_np(q, sb, st)
+    amax = np.abs(W).max()
+    assert st == np.float32(amax / 2688)
+    blk_scale = np.repeat(E4M3[sb], 16, axis=1) * st
+    # every element lies within half an E2M1 step (at most 1.0 at the top binade) of its
+    # block's grid, the block amax is covered by 6 * block scale up to E4M3 rounding
+    err = np.abs(W - D) / blk_scale
+    assert err.max() <= 1.0 + 1e-12
+    bmax = np.abs(W).reshape(16, -1, 16).max(axis=2)
+    assert np.all(bmax <= 6 * E4M3[sb] * st * (1 + 2**-4) + 1e-30)
+
+
+# ------------------------------------------------------------------------- router
+def test_router_vs_numpy_matmul_and_bias():
+    T, H, E = 5, 96, 17
+    x = bf16_bits(rng.normal(0, 1, (T, H)))
+    Wr = rng.normal(0, 0.02, (E, H)).astype(np.float32)
+    b = rng.normal(0, 1, E).astype(np.float32)
+    ref = bf16_val(x) @ Wr.astype(np.float64).T
+    np.testing.assert_allclose(oracle.router(x, Wr), ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.router(x, Wr, b), ref + b, rtol=1e-13, atol=1e-15)
+
+
+def test_router_one_hot_closed_form():
+    H, E = 64, 9
+    Wr = rng.normal(0, 1, (E, H)).astype(np.float32)
+    x = np.zeros((H, H), np.float32)
+    x[np.arange(H), np.arange(H)] = 1.0
+    l = oracle.router(bf16_bits(x), Wr)  # token h selects column h of Wr exactly
+    np.testing.assert_array_equal(l, Wr.T.astype(np.float64))
+
+
+# ------------------------------------------------------------------------- selection
+def brute_topk(l, k):
+    order = sorted(range(len(l)), key=lambda e: (-l[e], e))  # full sort, ties by index
+    return order[:k]
+
+
+def test_select_exhaustive_ties_and_signed_zero():
+    vals = [-1.0, -0.0, 0.0, 1.0]
+    for E in range(1, 5):
+        for combo in itertools.product(vals, repeat=E):
+            l = np.array([combo], np.float64)
+            for k in range(1, E + 1):
+                assert list(oracle.select(l, k)[0]) == brute_topk(list(combo), k)
+
+
+def test_select_random_small_and_full_size():
+    for _ in range(200):
+        E = int(rng.integers(1, 12))
+        k = int(rng.integers(1, E + 1))
+        l = rng.integers(-3, 4, (3, E)).astype(np.float64)  # many ties
+        ids = oracle.select(l, k)
+        for t in range(3):
+            assert list(ids[t]) == brute_topk(list(l[t]), k)
+    l = rng.normal(0, 1, (64, 256))
+    ids = oracle.select(l, 6)
+    ref = np.lexsort((np.tile(np.arange(256), (64, 1)), -l), axis=1)[:, :6]
+    np.testing.assert_array_equal(ids, ref)
+
+
+def test_select_rejects_nan_and_bad_k():
+    with pytest.raises(ValueError):
+        oracle.select(np.array([[0.0, np.nan, 1.0]]), 1)
+    with pytest.raises(ValueError):
+        oracle.select(np.zeros((1, 3)), 4)
+
+
+def test_six_plus_one_active_per_token():
+    # 256 routed experts, 6 chosen per token, all distinct and in range
+    l = rng.normal(0, 1, (100, 256))
+    ids = oracle.select(l, 6)
+    for row in ids:
+        assert len(set(row)) == 6 and all(0 <= e < 256 for e in row)
+
+
+# ------------------------------------------------------------------------- weights
+def test_weights_sum_to_one_and_closed_forms():
+    l = rng.normal(0, 2, (50, 32))
+    ids = oracle.select(l, 6)
+    w = oracle.weights(l, ids, True)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    s = scipy.special.expit(np.take_along_axis(l, ids, axis=1))
+    np.testing.assert_allclose(w, s / s.sum(axis=1, keepdims=True), rtol=1e-14)
+    np.testing.assert_allclose(oracle.weights(l, ids, False), s, rtol=1e-14)
+    # k = E: every expert is chosen, w_e = sigma_e / sum sigma
+    idsE = oracle.select(l, 32)
+    wE = oracle.weights(l, idsE, True)
+    sE = scipy.special.expit(l)
+    np.testing.assert_allclose(np.take_along_axis(sE / sE.sum(1, keepdims=True), idsE, 1), wE, rtol=1e-14)
+    # equal logits: w = 1/k;  logit 0: sigma = 1/2
+    z = np.zeros((1, 8))
+    np.testing.assert_allclose(oracle.weights(z, oracle.select(z, 4), True), 0.25, rtol=0, atol=1e-16)
+    np.testing.assert_array_equal(oracle.weights(z, oracle.select(z, 4), False), 0.5)
+
+
+# ------------------------------------------------------------------------- permute
+def test_permute_vs_stable_sort():
+    for T, E, k in [(1, 256, 6), (7, 5, 3), (300, 16, 4), (33, 256, 6)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        counts, offsets, sa, ap = oracle.permute(ids, E)
+        flat = ids.reshape(-1)
+        ref = sorted(range(T * k), key=lambda a: flat[a])  # Python's sort is stable
+        np.testing.assert_array_equal(sa, ref)
+        np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+        np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+        np.testing.assert_array_equal(sa[ap], np.arange(T * k))
+        assert counts.sum() == T * k
+
+
+# ------------------------------------------------------------------------- experts + combine
+def test_e1_k1_reduces_to_dense_swiglu():
+    T, H, I = 4, 64, 32
+    ex = make_bf16_experts(1, H, I, seed=1)
+    x = bf16_bits(rng.normal(0, 1, (T, H)))
+    ids = np.zeros((T, 1), np.int32)
+    w = oracle.weights(np.zeros((T, 1)), ids, True)
+    assert np.all(w == 1.0)
+    y = oracle.moe_tokens(ex, None, x, ids, w)
+    g, u, d = (bf16_val(ex.arrays[n][0]) for n in ("gate", "up", "down"))
+    for t in range(T):
+        np.testing.assert_allclose(y[t], dense_swiglu(bf16_val(x[t]), g, u, d), rtol=1e-12, atol=1e-14)
+
+
+def test_identity_experts_closed_form():
+    H = I = 32
+    c = 0.5
+    eye = bf16_bits(c * np.eye(H))[None]
+    ex = oracle.Experts(oracle.FMT_BF16, H, I, {"gate": eye, "up": eye, "down": eye})
+    x = bf16_bits(rng.normal(0, 2, (3, H)))
+    y = oracle.moe_tokens(ex, None, x, np.zeros((3, 1), np.int32), np.ones((3, 1)))
+    xv = bf16_val(x)
+    # g = u = c x, h = silu(c x) * c x, y = c h = c^3 x^2 sigmoid(c x)
+    np.testing.assert_allclose(y, c**3 * xv**2 * scipy.special.expit(c * xv), rtol=1e-14)
+
+
+def _layer_inputs(T, H, I, E, k, seed=0):
+    r = np.random.default_rng(seed)
+    x = bf16_bits(r.normal(0, 1, (T, H)))
+    Wr = r.normal(0, 0.05, (E, H)).astype(np.float32)
+    return x, Wr
+
+
+def test_identical_experts_make_routing_irrelevant():
+    T, H, I, E, k = 6, 64, 32, 8, 3
+    one = make_bf16_experts(1, H, I, seed=2)
+    routed = oracle.Experts(oracle.FMT_BF16, H, I,
+                            {n: np.repeat(one.arrays[n], E, axis=0) for n in ("gate", "up", "down")})
+    shared = make_bf16_experts(1, H, I, seed=3)
+    x, Wr = _layer_inputs(T, H, I, E, k)
+    out = oracle.moe_layer(x, Wr, routed, shared, k)
+    g, u, d = (bf16_val(one.arrays[n][0]) for n in ("gate", "up", "down"))
+    gs, us, ds = (bf16_val(shared.arrays[n][0]) for n in ("gate", "up", "down"))
+    for t in range(T):
+        xt = bf16_val(x[t])
+        ref = dense_swiglu(xt, gs, us, ds) + dense_swiglu(xt, g, u, d)
+        np.testing.assert_allclose(out["y"][t], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_zero_routed_down_leaves_shared_expert():
+    T, H, I, E, k = 5, 64, 32, 8, 2
+    routed = make_bf16_experts(E, H, I, seed=4)
+    routed.arrays["down"][:] = 0
+    routed = oracle.Experts(oracle.FMT_BF16, H, I, routed.arrays)
+    shared = make_bf16_experts(1, H, I, seed=5)
+    x, Wr = _layer_inputs(T, H, I, E, k, seed=6)
+    y = oracle.moe_layer(x, Wr, routed, shared, k)["y"]
+    gs, us, ds = (bf16_val(shared.arrays[n][0]) for n in ("gate", "up", "down"))
+    for t in range(T):
+        np.testing.assert_allclose(y[t], dense_swiglu(bf16_val(x[t]), gs, us, ds), rtol=1e-12)
+
+
+def test_routed_term_matches_explicit_weighted_sum():
+    # y - shared = sum_j w_j f_{e_j}(x), checked against per-expert dense SwiGLU in numpy
+    T, H, I, E, k = 4, 64, 32, 10, 3
+    routed = make_bf16_experts(E, H, I, seed=7)
+    shared = make_bf16_experts(1, H, I, seed=8)
+    x, Wr = _layer_inputs(T, H, I, E, k, seed=9)
+    out = oracle.moe_layer(x, Wr, routed, shared, k)
+    logits = bf16_val(x) @ Wr.astype(np.float64).T
+    for t in range(T):
+        xt = bf16_val(x[t])
+        top = brute_topk(list(logits[t]), k)
+        s = scipy.special.expit(logits[t][top])
+        ref = dense_swiglu(xt, *(bf16_val(shared.arrays[n][0]) for n in ("gate", "up", "down")))
+        for j, e in enumerate(top):
+            ref = ref + s[j] / s.sum() * dense_swiglu(xt, *(bf16_val(routed.arrays[n][e]) for n in ("gate", "up", "down")))
+        np.testing.assert_allclose(out["y"][t], ref, rtol=1e-11, atol=1e-13)
+
+
+def test_token_permutation_equivariance_and_scaling():
+    T, H, I, E, k = 12, 64, 32, 16, 4
+    routed = make_bf16_experts(E, H, I, seed=10)
+    shared = make_bf16_experts(1, H, I, seed=11)
+    x, Wr = _layer_inputs(T, H, I, E, k, seed=12)
+    base = oracle.moe_layer(x, Wr, routed, shared, k)
+    P = rng.permutation(T)
+    perm = oracle.moe_layer(x[P], Wr, routed, shared, k)
+    np.testing.assert_array_equal(perm["ids"], base["ids"][P])
+    np.testing.assert_array_equal(perm["y"], base["y"][P])
+    # doubling every down matrix doubles y exactly (bf16 x2 is exact)
+    r2 = dict(routed.arrays)
+    r2["down"] = bf16_bits(2 * bf16_val(routed.arrays["down"]))
+    s2 = dict(shared.arrays)
+    s2["down"] = bf16_bits(2 * bf16_val(shared.arrays["down"]))
+    dbl = oracle.moe_layer(x, Wr, oracle.Experts(0, H, I, r2), oracle.Experts(0, H, I, s2), k)
+    np.testing.assert_array_equal(dbl["y"], 2 * base["y"])
+
+
+def test_nvfp4_experts_equal_dense_on_dequantised_weights():
+    T, H, I, E, k = 3, 64, 32, 4, 2
+    arrays = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        qs, sbs, sts = [], [], []
+        for e in range(E):
+            q, sb, st = oracle.nvfp4_quantize(rng.normal(0, 0.02, (N, K)))
+            qs.append(q); sbs.append(sb); sts.append(st)
+        arrays["q_" + name] = np.stack(qs)
+        arrays["sb_" + name] = np.stack(sbs)
+        arrays["st_" + name] = np.array(sts, np.float32)
+    routed = oracle.Experts(oracle.FMT_NVFP4, H, I, arrays)
+    x, Wr = _layer_inputs(T, H, I, E, k, seed=13)
+    out = oracle.moe_layer(x, Wr, routed, None, k)
+    for t in range(T):
+        xt = bf16_val(x[t])
+        ref = np.zeros(H)
+        for j, e in enumerate(out["ids"][t]):
+            g, u, d = (dequant_np(arrays["q_" + n][e], arrays["sb_" + n][e], float(arrays["st_" + n][e]))
+                       for n in ("gate", "up", "down"))
+            ref += out["w"][t, j] * dense_swiglu(xt, g, u, d)
+        np.testing.assert_allclose(out["y"][t], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_zipf_constant_gives_half_the_assignments_to_16_experts():
+    # the stored workload constant, re-derived from the reference router and selection
+    vals = dict(l.split() for l in open(os.path.join(GOLDEN, "zipf_c.txt")) if not l.startswith("#"))
+    assert abs(float(vals["c"]) - dg.ZIPF_C) < 1e-12
+    T, H, E, k = 8192, 2048, 256, 6
+    x = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
+    Wr = dg.normal_f32((E, H), 0, dg.stream_id(0, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+    bias = dg.zipf_bias(E, dg.ZIPF_C)
+    ids = oracle.select(oracle.router(x, Wr, bias), k)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    share = np.sort(counts)[::-1][:16].sum() / (T * k)
+    assert 0.49 <= share <= 0.51
