@@ -1,0 +1,237 @@
+// gemm.hip -- grouped expert GEMMs for larger batches (T > 32 tokens) and the combine.
+//
+// Prefill is compute-heavy rather than weight-bound (recipes.vllm.ai "RecursiveSI/flint",
+// Benchmarking: the NVFP4 checkpoint barely changes the 8K-token prefill time), so the
+// expert FFNs run on bf16 MFMA with fp32 accumulation, LDS-staged tiles and a register
+// prefetch of the next K step.
+//
+// Work items come from the device plan: one item = (touched expert, 128-row tile of its
+// slots).  Gate/up: A = the expert's tokens gathered from x, B = 32 gate rows and the same
+// 32 up rows per wave column, epilogue h = bf16(silu(g) * u).  Down: A = h rows of the
+// expert's slots (contiguous), epilogue o = bf16(acc).  The combine then forms
+// y = o_shared + sum_j w_j o_j per token, in that fixed order.
+#include "common.h"
+
+namespace flint {
+
+namespace {
+
+constexpr int BM = kGemmBM;  // rows (slots) per tile
+constexpr int BN = 128;      // B rows per tile
+constexpr int BK = 64;       // K per stage
+constexpr int LDP = BK + 8;  // padded LDS row (bf16 elements): 144 bytes
+
+__device__ __forceinline__ u32x4 ld16g(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+template <int MODE, int FMT>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, int E, int k,
+                                                           WSet w,
+                                                           const uint16_t *__restrict__ asrc,
+                                                           const int32_t *__restrict__ sa,
+                                                           Plan p, uint16_t *__restrict__ out)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
+    const int item = blockIdx.x;
+    if (item >= p.meta[1]) return;
+    const int code = p.items[item];
+    const int u = code >> 16, mtile = code & 0xffff;
+    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    const bool sh = (e == E);
+    const int m0 = mtile * BM;
+    const int valid = min(BM, cnt - m0);
+    const int nb = blockIdx.y;
+    const int K = MODE == 0 ? H : I;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Each thread stages 4 A rows and 4 B rows (one 16-byte chunk of each per stage).
+    const int srow = tid >> 3, schunk = tid & 7;
+    const uint16_t *arow[4];
+    const uint8_t *brow[4];
+    const uint8_t *bsf[4];
+    float bts[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int rr = srow + 32 * j;
+        const int ri = min(rr, valid - 1);
+        if (MODE == 0) {
+            const int tok = sh ? m0 + ri : sa[base + m0 + ri] / k;
+            arow[j] = asrc + (size_t)tok * H;
+        } else {
+            arow[j] = asrc + (size_t)(base + m0 + ri) * I;
+        }
+        // B row rr of the tile
+        const WMat *mat;
+        int n;
+        if (MODE == 0) {
+            const int wcol = rr >> 6, within = rr & 63;
+            mat = (within >> 5) ? &w.up : &w.gate;
+            n = nb * 64 + wcol * 32 + (within & 31);
+        } else {
+            mat = &w.down;
+            n = nb * BN + rr;
+        }
+        if (FMT == 0) {
+            const size_t mb = (size_t)H * I * 2;
+            brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * K * 2;
+            bsf[j] = nullptr;
+            bts[j] = 1.f;
+        } else {
+            const size_t mb = (size_t)H * I / 2, sb = (size_t)H * I / 16;
+            brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2);
+            bsf[j] = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * (K / 16);
+            bts[j] = sh ? *mat->ts_shared : mat->ts_routed[e];
+        }
+    }
+    (void)bts;
+
+    u32x4 ra[4], rb[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            ra[j] = ld16g(arow[j] + k0 + schunk * 8);
+            if (FMT == 0) {
+                rb[j] = ld16g(brow[j] + (size_t)(k0 + schunk * 8) * 2);
+            } else {
+                const int kk = k0 + schunk * 8;
+                uint32_t q = *reinterpret_cast<const uint32_t *>(brow[j] + kk / 2);
+                float s = e4m3_to_f32(bsf[j][kk / 16]);
+                rb[j] = dequant8(q, s);
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            *reinterpret_cast<u32x4 *>(&As[buf][srow + 32 * j][schunk * 8]) = ra[j];
+            *reinterpret_cast<u32x4 *>(&Bs[buf][srow + 32 * j][schunk * 8]) = rb[j];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int ms = 0; ms < 4; ms++)
+                af[ms] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&As[buf][wm * 64 + ms * 16 + r][kk * 32 + g * 8]));
+#pragma unroll
+            for (int ns = 0; ns < 4; ns++)
+                bfr[ns] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bs[buf][wn * 64 + ns * 16 + r][kk * 32 + g * 8]));
+#pragma unroll
+            for (int ms = 0; ms < 4; ms++)
+#pragma unroll
+                for (int ns = 0; ns < 4; ns++) acc[ms][ns] = mfma16x16x32(af[ms], bfr[ns], acc[ms][ns]);
+        }
+        if (kt + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.  acc[ms][ns][i] = D[row = wm*64 + ms*16 + 4g + i][brow = wn*64 + ns*16 + r].
+    float tsg = 1.f, tsu = 1.f, tsd = 1.f;
+    if (FMT == 1) {
+        tsg = sh ? *w.gate.ts_shared : w.gate.ts_routed[e];
+        tsu = sh ? *w.up.ts_shared : w.up.ts_routed[e];
+        tsd = sh ? *w.down.ts_shared : w.down.ts_routed[e];
+    }
+#pragma unroll
+    for (int ms = 0; ms < 4; ms++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = wm * 64 + ms * 16 + 4 * g + i;
+            if (row >= valid) continue;
+            const size_t slot = (size_t)(base + m0 + row);
+            if (MODE == 0) {
+#pragma unroll
+                for (int ns = 0; ns < 2; ns++) {
+                    const int col = nb * 64 + wn * 32 + ns * 16 + r;
+                    const float gv = acc[ms][ns][i] * tsg, uv = acc[ms][ns + 2][i] * tsu;
+                    out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
+                }
+            } else {
+#pragma unroll
+                for (int ns = 0; ns < 4; ns++) {
+                    const int col = nb * BN + wn * 64 + ns * 16 + r;
+                    out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i] * tsd);
+                }
+            }
+        }
+    }
+}
+
+// y[t][n] = bf16(o[T*k + t][n] + sum_j w[t][j] * o[ap[t*k + j]][n]); 8 columns per thread.
+__global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int S,
+                                                      const uint16_t *__restrict__ o,
+                                                      const float *__restrict__ topk_w,
+                                                      const int32_t *__restrict__ ap,
+                                                      uint16_t *__restrict__ y)
+{
+    const int per_tok = H / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)T * per_tok) return;
+    const int t = (int)(gid / per_tok), c = (int)(gid % per_tok) * 8;
+    float acc[8];
+    if (S) {
+        u32x4 v = ld16g(o + ((size_t)T * k + t) * H + c);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc[2 * i] = bf2f(v[i] & 0xffffu);
+            acc[2 * i + 1] = bf2f(v[i] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] = 0.f;
+    }
+    for (int j = 0; j < k; j++) {
+        const float wj = topk_w[t * k + j];
+        u32x4 v = ld16g(o + (size_t)ap[t * k + j] * H + c);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc[2 * i] += wj * bf2f(v[i] & 0xffffu);
+            acc[2 * i + 1] += wj * bf2f(v[i] >> 16);
+        }
+    }
+    u32x4 outv;
+#pragma unroll
+    for (int i = 0; i < 4; i++) outv[i] = f2bf(acc[2 * i]) | (f2bf(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4 *>(y + (size_t)t * H + c) = outv;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
+                               const float *topk_w, const int32_t *sa, const int32_t *ap,
+                               const Plan &plan, uint16_t *h, uint16_t *o, uint16_t *y,
+                               hipStream_t st)
+{
+    const int64_t slots = T * s.k + T * s.S;
+    const int64_t max_items = (slots + kGemmBM - 1) / kGemmBM + s.E + s.S;
+    dim3 g1((unsigned)max_items, (unsigned)(s.I / 64));
+    dim3 g2((unsigned)max_items, (unsigned)(s.H / BN));
+    if (w.fmt == 0) {
+        grouped_gemm_kernel<0, 0><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        grouped_gemm_kernel<1, 0><<<g2, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+    } else {
+        grouped_gemm_kernel<0, 1><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        grouped_gemm_kernel<1, 1><<<g2, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+    }
+    const int64_t nthreads = T * (s.H / 8);
+    combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o,
+                                                                       topk_w, ap, y);
+    return hipGetLastError();
+}
+
+}  // namespace flint

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every symbol include/flint_moe.h declares, and
+rejects invalid arguments with the documented status codes before touching the device
+(no GPU is needed: every call here fails validation, so no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_transformer_wave_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flint_moe.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(flint_moe_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) == set(fm.EXPORTED)
+    L = ctypes.CDLL(fm.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(7):
+        assert isinstance(fm.status_string(s), str) and fm.status_string(s)
+    assert fm.status_string(99) == "unknown status"
+
+
+A = 1 << 20          # a fake, 16-byte aligned address (never dereferenced)
+MIS = A + 8          # misaligned
+
+
+def _route(d, T, x=A, wr=A, bias=None, logits=None, ids=A, w=A, flags=0, ws=None, nb=0):
+    L = fm.lib()
+    return L.flint_moe_route(None if d is None else ctypes.byref(d), T, x, wr, bias, logits,
+                             ids, w, flags, ws, nb, None)
+
+
+def test_route_validation():
+    d = fm.desc(2048, 768)
+    assert _route(None, 1) == fm.ERR_NULL
+    assert _route(fm.desc(2048, 768, n_experts=0), 1) == fm.ERR_SHAPE
+    assert _route(fm.desc(2048, 768, n_experts=300), 1) == fm.ERR_SHAPE
+    assert _route(fm.desc(2048, 768, top_k=9), 1) == fm.ERR_SHAPE
+    assert _route(fm.desc(2048, 768, n_experts=4, top_k=5), 1) == fm.ERR_SHAPE
+    assert _route(fm.desc(2000, 768), 1) == fm.ERR_SHAPE
+    assert _route(fm.desc(2048, 700), 1) == fm.ERR_SHAPE
+    assert _route(fm.desc(2048, 768, n_shared=2), 1) == fm.ERR_SHAPE
+    assert _route(d, -1) == fm.ERR_SHAPE
+    assert _route(d, 70000) == fm.ERR_SHAPE
+    assert _route(d, 0) == fm.OK
+    assert _route(d, 1, x=None) == fm.ERR_NULL
+    assert _route(d, 1, ids=None) == fm.ERR_NULL
+    assert _route(d, 1, x=MIS) == fm.ERR_ALIGN
+    assert _route(d, 1, flags=4) == fm.ERR_FORMAT
+    assert _route(d, 1, flags=fm.ROUTE_LOGITS_IN) == fm.ERR_NULL   # logits missing
+    assert _route(d, 1) == fm.ERR_NULL                              # no logits, no workspace
+    assert _route(d, 1, ws=A, nb=16) == fm.ERR_WORKSPACE
+
+
+def _weights(fmt=fm.WFMT_BF16, shared=True, scales=False, **kw):
+    w = fm.Weights(fmt, A, A, A, *( (A, A, A) if shared else (None, None, None)))
+    if scales:
+        for n in ("gate_sf", "up_sf", "down_sf", "gate_ts", "up_ts", "down_ts"):
+            setattr(w, n, A)
+        if shared:
+            for n in ("sh_gate_sf", "sh_up_sf", "sh_down_sf", "sh_ts"):
+                setattr(w, n, A)
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w.c_struct()
+
+
+def _forward(d, w, T, ws=A, nb=0, **kw):
+    args = dict(x=A, ids=A, tw=A, off=A, sa=A, ap=A, y=A)
+    args.update(kw)
+    return fm.lib().flint_moe_forward(ctypes.byref(d), ctypes.byref(w), T, args["x"], args["ids"],
+                                      args["tw"], args["off"], args["sa"], args["ap"], args["y"],
+                                      ws, nb, None)
+
+
+def test_forward_and_layer_validation():
+    d = fm.desc(2048, 768)
+    need = fm.workspace_bytes(d, 8)
+    assert need > 0 and fm.workspace_bytes(d, 16) > need
+    assert fm.workspace_bytes(d, -1) == 0 and fm.workspace_bytes(fm.desc(100, 768), 1) == 0
+    assert fm.workspace_bytes(d, 8, 7) == 0
+    assert _forward(d, _weights(), 0) == fm.OK
+    assert _forward(d, _weights(), 8, nb=need - 1) == fm.ERR_WORKSPACE
+    assert _forward(d, _weights(), 8, nb=need, y=None) == fm.ERR_NULL
+    assert _forward(d, _weights(), 8, nb=need, sa=MIS) == fm.ERR_ALIGN
+    assert _forward(d, _weights(fmt=3), 8, nb=need) == fm.ERR_FORMAT
+    assert _forward(d, _weights(shared=False), 8, nb=need) == fm.ERR_NULL
+    assert _forward(fm.desc(2048, 768, n_shared=0), _weights(), 8, nb=need) == fm.ERR_FORMAT
+    assert _forward(d, _weights(scales=True), 8, nb=need) == fm.ERR_FORMAT   # bf16 with scales
+    assert _forward(d, _weights(fmt=fm.WFMT_NVFP4), 8, nb=need) == fm.ERR_FORMAT  # nvfp4 without
+    assert _forward(d, _weights(fmt=fm.WFMT_NVFP4, scales=True, gate_ts=MIS), 8, nb=need) == fm.ERR_ALIGN
+    assert _forward(d, _weights(gate=MIS), 8, nb=need) == fm.ERR_ALIGN
+    L = fm.lib()
+    w = _weights()
+    assert L.flint_moe_layer(ctypes.byref(d), ctypes.byref(w), 0, A, A, None, A, None, A, 0, None) == fm.OK
+    assert L.flint_moe_layer(ctypes.byref(d), ctypes.byref(w), 4, A, None, None, A, None, A, need, None) == fm.ERR_NULL
+    assert L.flint_moe_layer(ctypes.byref(d), ctypes.byref(w), 4, A, A, None, A, None, A, 16, None) == fm.ERR_WORKSPACE
+    assert L.flint_moe_permute(ctypes.byref(d), 4, A, A, None, A, A, None, 0, None) == fm.ERR_NULL
+    assert L.flint_moe_permute(ctypes.byref(d), 0, None, None, None, None, None, None, 0, None) == fm.OK

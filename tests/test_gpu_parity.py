@@ -1,0 +1,160 @@
+"""GPU parity: the HIP library (through the C ABI) against the reference on the same
+seeded bytes.  See tests/moe_cases.py for the two-stage protocol and tolerances."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import sparse_moe_transformer_wave_amd as fm  # noqa: E402
+from sparse_moe_transformer_wave_amd import datagen as dg  # noqa: E402
+from moe_cases import Case, check_forward, check_routing  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _parity(c, steps=False, tokens=None):
+    _say("case T=%d H=%d I=%d E=%d k=%d S=%d fmt=%d" % (c.T, c.H, c.I, c.E, c.k, c.S, c.fmt))
+    c.upload()
+    g = c.run_steps() if steps else c.run_layer()
+    rep = {}
+    w64 = check_routing(c, g, rep)
+    rm, rl = check_forward(c, g, w64, tokens)
+    _say("  ok: max rel %.2e, rel L1 %.2e, near ties %s" % (rm, rl, rep.get("near_ties")))
+    return g
+
+
+# ---------------------------------------------------------------- tiny layer (H=256, I=128)
+@pytest.mark.parametrize("T", [32, 1, 3, 8, 17, 31])
+def test_tiny_streaming_path(T):
+    _parity(Case(T, 256, 128, 256, 6))
+
+
+@pytest.mark.parametrize("T", [33, 100, 257, 1000])
+def test_tiny_grouped_gemm_path(T):
+    _parity(Case(T, 256, 128, 256, 6))
+
+
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_tiny_three_call_path(T):
+    _parity(Case(T, 256, 128, 256, 6), steps=True)
+
+
+@pytest.mark.parametrize("T,E,k,S,renorm", [
+    (5, 1, 1, 0, 1), (40, 1, 1, 1, 1), (7, 8, 8, 1, 1), (50, 8, 8, 0, 1),
+    (9, 16, 4, 0, 0), (64, 16, 4, 1, 0), (3, 256, 8, 1, 1)])
+def test_edge_shapes(T, E, k, S, renorm):
+    _parity(Case(T, 256, 128, E, k, S=S, renorm=renorm))
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 40, 200])
+def test_tiny_nvfp4(T):
+    _parity(Case(T, 256, 128, 256, 6, fmt=fm.WFMT_NVFP4))
+
+
+def test_zero_tokens_is_a_noop():
+    c = Case(1, 256, 128, 256, 6).upload()
+    y = torch.full((1, 256), 7, dtype=torch.int16, device="cuda")
+    ws = c.workspace(1)
+    fm.layer(c.desc, c.weights, 0, c.d_x, c.d_Wr, None, y, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7)
+
+
+# ---------------------------------------------------------------- invariants on the GPU
+def test_determinism_duplicates_scaling_permutation():
+    T, H, I = 48, 256, 128
+    x = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), 1.0)
+    x[7] = x[3]
+    x[40] = x[3]
+    for Tn in (T, 20):  # grouped-GEMM path and streaming path
+        xs = np.ascontiguousarray(x[:Tn])
+        c = Case(Tn, H, I, 256, 6, x=xs).upload()
+        a, b = c.run_layer(), c.run_layer()
+        np.testing.assert_array_equal(a["y"], b["y"])  # run-to-run bitwise
+        np.testing.assert_array_equal(a["y"][7], a["y"][3])  # duplicate tokens bitwise
+        if Tn > 40:
+            np.testing.assert_array_equal(a["y"][40], a["y"][3])
+        c2 = Case(Tn, H, I, 256, 6, x=xs, wscale=2.0).upload()
+        d = c2.run_layer()
+        np.testing.assert_array_equal(dg.bf16_bits_to_f32(d["y"]), 2 * dg.bf16_bits_to_f32(a["y"]))
+        P = np.random.default_rng(5).permutation(Tn)
+        c3 = Case(Tn, H, I, 256, 6, x=np.ascontiguousarray(xs[P])).upload()
+        p = c3.run_layer()
+        np.testing.assert_array_equal(p["topk_ids"], a["topk_ids"][P])
+        ya, yp = dg.bf16_bits_to_f32(a["y"][P]), dg.bf16_bits_to_f32(p["y"])
+        assert np.abs(ya - yp).max() <= 2e-2 * np.abs(ya).max()
+        _say("permutation: bitwise equal rows %d of %d" % (int((a["y"][P] == p["y"]).all(1).sum()), Tn))
+
+
+def test_route_logits_in_ties_signed_zero_nan():
+    E, k, T = 256, 6, 64
+    rng = np.random.default_rng(3)
+    lg = rng.integers(-2, 3, (T, E)).astype(np.float32)  # heavy ties
+    lg[0, :] = 0.0
+    lg[1, ::2] = -0.0
+    lg[2, 5] = np.nan
+    lg[2, 9] = -np.inf
+    lg[3, :] = -np.inf
+    lg[3, 200] = np.nan
+    d = fm.desc(256, 128, E, k, 1, 1)
+    dl = torch.from_numpy(lg).cuda()
+    ids = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fm.workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    fm.route(d, T, None, None, None, ids, w, ws, logits=dl, logits_in=True)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    ref_in = lg.astype(np.float64)
+    ref_in[np.isnan(ref_in)] = -np.inf  # reading: NaN orders below -inf; rows 2, 3 checked by hand
+    for t in range(T):
+        if t in (2, 3):
+            continue
+        order = sorted(range(E), key=lambda e: (-ref_in[t, e], e))[:k]
+        assert list(got[t]) == order
+    # row 2: NaN at 5 ranks last, -inf at 9 next to last: top-6 are the 6 largest finite
+    order2 = sorted([e for e in range(E) if e not in (5, 9)], key=lambda e: (-lg[2, e], e))[:k]
+    assert list(got[2]) == order2
+    # row 3: all -inf except a NaN: lowest indices 0..5 (the NaN, expert 200, is last)
+    assert list(got[3]) == [0, 1, 2, 3, 4, 5]
+
+
+# ---------------------------------------------------------------- full-size layer
+_FULL = {}
+
+
+def _full_case(T, fmt=fm.WFMT_BF16, bias_c=None):
+    H, I, E, k = 2048, 768, 256, 6
+    if fmt == fm.WFMT_BF16:
+        return Case(T, H, I, E, k, bias_c=bias_c)
+    # NVFP4: quantise only the experts the reference routing touches; the others hold
+    # zero codes, identically on both sides.
+    x = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), 1.0)
+    Wr = dg.normal_f32((E, H), 0, dg.stream_id(0, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+    ids = oracle.select(oracle.router(x, Wr), k)
+    return Case(T, H, I, E, k, fmt=fmt, experts=sorted(set(ids.reshape(-1).tolist())))
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_full_decode_bf16(T):
+    _parity(_full_case(T))
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_full_decode_nvfp4(T):
+    _parity(_full_case(T, fmt=fm.WFMT_NVFP4))
+
+
+@pytest.mark.parametrize("zipf", [False, True])
+def test_full_prefill_8192(zipf):
+    c = _full_case(8192, bias_c=dg.ZIPF_C if zipf else None)
+    toks = np.unique(np.concatenate([np.arange(0, 8192, 523), [8191]])).astype(np.int64)
+    _parity(c, tokens=toks)
