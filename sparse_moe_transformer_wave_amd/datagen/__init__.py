@@ -159,3 +159,51 @@ class LayerInputs:
         return (normal_f64((I, H), s, stream_id(L, KIND_GATE, e), W_STD),
                 normal_f64((I, H), s, stream_id(L, KIND_UP, e), W_STD),
                 normal_f64((H, I), s, stream_id(L, KIND_DOWN, e), W_STD))
+
+
+# ----------------------------------------------------------------------------- device side
+_dev = None
+_DEV_SO = os.path.join(_HERE, "libflint_gen_device.so")
+
+
+def _D():
+    global _dev
+    if _dev is None:
+        if not os.path.exists(_DEV_SO):
+            raise RuntimeError("libflint_gen_device.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(_DEV_SO)
+        vp, i64, u64, d = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
+        L.flint_gen_normal_bf16.argtypes = [vp, i64, i64, u64, u64, d, vp]
+        L.flint_gen_normal_f32.argtypes = [vp, i64, u64, u64, d, vp]
+        L.flint_gen_nvfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, u64, u64, d, vp]
+        for f in ("flint_gen_normal_bf16", "flint_gen_normal_f32", "flint_gen_nvfp4"):
+            getattr(L, f).restype = ctypes.c_int
+        _dev = L
+    return _dev
+
+
+def _cur_stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def device_normal_bf16(t, n_mat: int, per_mat: int, seed: int, stream0: int, std: float):
+    """Fill device tensor t (>= n_mat * per_mat bf16) with matrices of streams stream0 + m."""
+    assert t.numel() * t.element_size() >= n_mat * per_mat * 2
+    rc = _D().flint_gen_normal_bf16(t.data_ptr(), n_mat, per_mat, seed, stream0, std, _cur_stream())
+    if rc:
+        raise RuntimeError("flint_gen_normal_bf16 failed: %d" % rc)
+
+
+def device_normal_f32(t, seed: int, stream: int, std: float):
+    rc = _D().flint_gen_normal_f32(t.data_ptr(), t.numel(), seed, stream, std, _cur_stream())
+    if rc:
+        raise RuntimeError("flint_gen_normal_f32 failed: %d" % rc)
+
+
+def device_nvfp4(q, sf, ts, scratch, n_mat: int, N: int, K: int, seed: int, stream0: int,
+                 std: float):
+    rc = _D().flint_gen_nvfp4(q.data_ptr(), sf.data_ptr(), ts.data_ptr(), scratch.data_ptr(),
+                              n_mat, N, K, seed, stream0, std, _cur_stream())
+    if rc:
+        raise RuntimeError("flint_gen_nvfp4 failed: %d" % rc)
