@@ -220,12 +220,13 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
 
 static int forward_impl(const Shape &s, const WSet &wset, int64_t T, const uint16_t *x,
                         const float *topk_w, const int32_t *sa, const int32_t *ap, uint16_t *y,
-                        void *ws, const WsLayout &L, const Plan &plan, hipStream_t st)
+                        void *ws, const WsLayout &L, const Plan &plan, hipStream_t st,
+                        const RouteOut *route = nullptr)
 {
     char *b = (char *)ws;
     if (T <= kGemvMaxT) {
         return hip_status(launch_gemv_forward(s, wset, T, x, topk_w, sa, ap, plan,
-                                              (float *)(b + L.h), (float *)(b + L.o), y, st));
+                                              (uint16_t *)(b + L.h), y, route, st));
     }
     return hip_status(launch_gemm_forward(s, wset, T, x, topk_w, sa, ap, plan,
                                           (uint16_t *)(b + L.h), (uint16_t *)(b + L.o), y, st));
@@ -296,10 +297,19 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     const Plan plan = plan_view(ws, L, s);
     rc = hip_status(launch_router(s, T, x, w_router, logit_bias, lg, st));
     if (rc) return rc;
-    rc = hip_status(launch_topk(s, T, lg, ids, tw, st));
-    if (rc) return rc;
-    rc = hip_status(launch_permute(s, T, ids, cnt, off, sa, ap, &plan, st));
-    if (rc) return rc;
+    if (T <= kFusedSelectMaxT) {
+        const RouteOut ro{lg, ids, tw, cnt, off, sa, ap};
+        return forward_impl(s, wset_of(weights), T, x, tw, sa, ap, y, ws, L, plan, st, &ro);
+    }
+    if (T <= kGemvMaxT) {
+        rc = hip_status(launch_select_permute(s, T, lg, ids, tw, cnt, off, sa, ap, plan, st));
+        if (rc) return rc;
+    } else {
+        rc = hip_status(launch_topk(s, T, lg, ids, tw, st));
+        if (rc) return rc;
+        rc = hip_status(launch_permute(s, T, ids, cnt, off, sa, ap, &plan, st));
+        if (rc) return rc;
+    }
     return forward_impl(s, wset_of(weights), T, x, tw, sa, ap, y, ws, L, plan, st);
 }
 

@@ -71,9 +71,23 @@ hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t
                           hipStream_t st);
 hipError_t launch_plan(const Shape &s, int64_t T, const int32_t *offsets, const Plan &plan,
                        hipStream_t st);
+// T <= kGemvMaxT: top-k, grouping and plan in one workgroup.
+hipError_t launch_select_permute(const Shape &s, int64_t T, const float *logits, int32_t *ids,
+                                 float *w, int32_t *counts, int32_t *offsets, int32_t *sa,
+                                 int32_t *ap, const Plan &plan, hipStream_t st);
+// Routing outputs a fused small-batch launch writes (workgroup 0) for later kernels.
+struct RouteOut {
+    const float *logits;
+    int32_t *ids;
+    float *w;
+    int32_t *counts, *offsets, *sa, *ap;
+};
+// Streaming path.  With `route` non-null (T <= kFusedSelectMaxT), the gate/up kernel
+// selects and groups from route->logits itself; otherwise the plan must already exist.
+constexpr int kFusedSelectMaxT = 8;
 hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
-                               const Plan &plan, float *h, float *o32, uint16_t *y,
+                               const Plan &plan, uint16_t *h, uint16_t *y, const RouteOut *route,
                                hipStream_t st);
 hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
@@ -134,11 +148,141 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t q, float scale)
     return r;
 }
 
+// Wave-wide reductions with DPP: xor-1 and xor-2 quad permutes, then the half-row and
+// row mirrors leave every lane of a 16-lane row with the row's result; the four row
+// results are read back as scalars.  A fixed combination order keeps sums deterministic.
+#define FLINT_DPP(v, ctrl) __builtin_amdgcn_update_dpp((v), (v), (ctrl), 0xf, 0xf, false)
 __device__ __forceinline__ float wave_sum(float v)
 {
+    v += __int_as_float(FLINT_DPP(__float_as_int(v), 0xB1));   // quad_perm [1,0,3,2]
+    v += __int_as_float(FLINT_DPP(__float_as_int(v), 0x4E));   // quad_perm [2,3,0,1]
+    v += __int_as_float(FLINT_DPP(__float_as_int(v), 0x141));  // row_half_mirror
+    v += __int_as_float(FLINT_DPP(__float_as_int(v), 0x140));  // row_mirror
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0xB1));
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0x4E));
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0x141));
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0x140));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// ---- top-k of one token (one wave) --------------------------------------------------
+// Order-preserving 64-bit key: high word = monotone image of the fp32 logit (-0 mapped to
+// +0, NaN below -inf), low word = 0xffff - e so that equal logits prefer the lower index.
+__device__ __forceinline__ uint64_t select_key(float v, int e)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t ord;
+    if ((u & 0x7fffffffu) > 0x7f800000u) ord = 0u;           // NaN: below everything
+    else if (u == 0x80000000u) ord = 0x80000000u;              // -0 == +0
+    else ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint64_t)(0xffffu - (uint32_t)e);
+}
+
+// 64-bit max as two 32-bit DPP maxima: the high words, then the low words of the lanes
+// whose high word is the maximum.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+    return ((uint64_t)mh << 32) | ml;
+}
+
+// Called by a whole wave.  Each lane holds experts lane, lane+64, lane+128, lane+192;
+// k rounds of a wave-wide arg-max, the winning lane retires its entry.  Lane 0 writes
+// ids[0..k) and the sigmoid weights (renormalised to sum 1 if renorm).
+__device__ __forceinline__ void topk_token(const float *__restrict__ lg, int E, int k, int renorm,
+                                           int32_t *__restrict__ ids, float *__restrict__ wout)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t key[4];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    for (int i = 0; i < 4; i++) {
+        int e = lane + 64 * i;
+        key[i] = (e < E) ? select_key(lg[e], e) : 0ull;
+    }
+    int sel_id[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        if (j >= k) break;
+        uint64_t m = key[0];
+#pragma unroll
+        for (int i = 1; i < 4; i++) m = key[i] > m ? key[i] : m;
+        uint64_t best = wave_max_u64(m);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (key[i] == best) key[i] = 0ull;
+        sel_id[j] = (int)(0xffffu - (uint32_t)(best & 0xffffu));
+    }
+    if (lane == 0) {
+        float sg[8];
+        float sum = 0.f;
+        for (int j = 0; j < k; j++) {
+            sg[j] = 1.0f / (1.0f + expf(-lg[sel_id[j]]));
+            sum += sg[j];
+        }
+        for (int j = 0; j < k; j++) {
+            ids[j] = sel_id[j];
+            wout[j] = renorm ? sg[j] / sum : sg[j];
+        }
+    }
+}
+
+// ---- grouping of at most 64 assignments by one wave ---------------------------------
+// ids[a] (a < n <= 64) are expert ids.  Computes, in the order of a stable sort by expert:
+// slot_of[a] (position of a), and the touched-expert list (ascending id, then the shared
+// expert E with all T tokens when S): touched[u], tbase[u] (first slot), tcount[u].
+// Returns the list length (wave-uniform).
+__device__ __forceinline__ int wave_group_small(int n, int T, int k, int E, int S,
+                                                const int32_t *ids, int *touched, int *tbase,
+                                                int *tcount, int *slot_of)
+{
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < n;
+    const int e = valid ? ids[lane] : 0x7fffffff;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 9; b++) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t vote = __ballot(bit);
+        peers &= bit ? vote : ~vote;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & lt), size = __popcll(peers);
+    const bool leader = valid && rank == 0;
+    const uint64_t lmask = __ballot(leader);
+    int below = 0, lead_below = 0;
+    for (int j = 0; j < n; j++) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        below += (ej < e);
+        lead_below += (int)((lmask >> j) & 1ull) & (int)(ej < e);
+    }
+    if (valid) slot_of[lane] = below + rank;
+    if (leader) {
+        touched[lead_below] = e;
+        tbase[lead_below] = below;
+        tcount[lead_below] = size;
+    }
+    const int nr = __popcll(lmask);
+    if (S && lane == 0) {
+        touched[nr] = E;
+        tbase[nr] = T * k;
+        tcount[nr] = T;
+    }
+    return nr + S;
 }
 
 }  // namespace flint

@@ -2,17 +2,21 @@
 //
 // Decode reads every touched expert's weights once from HBM; the cost of a step is the
 // active weights, not the checkpoint (qantcore.space review, section 01).  Weights stream
-// straight from HBM into MFMA B operands with 16-byte loads (no LDS staging, no reuse to
-// exploit); the expert's tokens (<= 32, two 16-row MFMA tiles) form the A operand and
-// come from L2.  The shared expert is one more entry of the touched-expert list
-// (news.ditty.ir, third paragraph: one shared expert always active).
+// straight from HBM into MFMA B operands with 16-byte loads, all of a wave's loads issued
+// before the first MFMA; the expert's tokens (<= 32, one or two 16-row MFMA tiles) form
+// the A operand and come from L2.  The shared expert is one more entry of the
+// touched-expert list (news.ditty.ir, third paragraph: one shared expert always active).
 //
-// Pass 1 (gate/up): one workgroup per (touched expert, 16 rows of I); its 4 waves split
-//   K and meet in LDS; h = silu(g) * u is stored in fp32.
-// Pass 2 (down + combine): one workgroup per (touched expert, 16 rows of H); the fp32 h
-//   enters the bf16 MFMA as hi + lo parts, so it keeps ~16 significant bits.  Per-slot
-//   outputs go to an fp32 buffer; the last workgroup to finish a 16-row block of H
-//   combines it (shared first, then the k routed slots in order) and writes bf16 y.
+// Pass 1 (gate/up): one workgroup per (touched expert, 8 rows of I).  Its B operand holds
+//   8 gate rows in MFMA columns 0-7 and the same 8 up rows in columns 8-15, so one MFMA
+//   produces g and u side by side; the 4 waves split K and meet in LDS; h = silu(g) * u is
+//   rounded to bf16.  For T <= 8 every workgroup first selects and groups the tokens'
+//   experts itself from the router logits (a few hundred instructions), which saves the
+//   launch of a separate routing kernel; workgroup 0 publishes the routing tensors.
+// Pass 2 (down + combine): one workgroup per 16 rows of H, covering every touched expert
+//   (one wave per expert at a time, all of its weight and h loads in flight together).
+//   Per-slot outputs stay in LDS in fp32 and the workgroup combines them (shared first,
+//   then the k routed slots in order) into bf16 y, so no other workgroup is waited for.
 #include "common.h"
 
 #include <algorithm>
@@ -34,270 +38,342 @@ __device__ __forceinline__ float expert_ts(const WMat &m, int e, int E)
     return e == E ? *m.ts_shared : m.ts_routed[e];
 }
 
-// fp32 x8 -> (hi, lo) bf16 x8 with hi = rne(v), lo = rne(v - hi).
-__device__ __forceinline__ void split_bf16x8(const float *v, u32x4 &hi, u32x4 &lo)
+// ------------------------------------------------------------------ pass 1: gate / up
+// Top-k of the T <= 8 tokens (wave t takes tokens t, t + 4) and their grouping, in LDS.
+// Workgroup 0 also writes the routing tensors and the plan for the down pass.
+struct FusedRoute {
+    int32_t ids[64];
+    float w[64];
+    int slot[64];
+    int touched[72], tbase[72], tcount[72];
+    int nT;
+};
+
+__device__ void fused_select(int T, int E, int k, int S, int renorm, const RouteOut &ro,
+                             const Plan &p, FusedRoute &fr)
 {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t h0 = f2bf(v[2 * i]), h1 = f2bf(v[2 * i + 1]);
-        uint32_t l0 = f2bf(v[2 * i] - bf2f(h0)), l1 = f2bf(v[2 * i + 1] - bf2f(h1));
-        hi[i] = h0 | (h1 << 16);
-        lo[i] = l0 | (l1 << 16);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int t = wave; t < T; t += 4)
+        topk_token(ro.logits + (size_t)t * E, E, k, renorm, fr.ids + t * k, fr.w + t * k);
+    __syncthreads();
+    if (wave == 0) {
+        const int nT = wave_group_small(T * k, T, k, E, S, fr.ids, fr.touched, fr.tbase, fr.tcount, fr.slot);
+        if (lane == 0) fr.nT = nT;
     }
+    __syncthreads();
+    if (blockIdx.x != 0) return;
+    const int n = T * k;
+    for (int a = tid; a < n; a += 256) {
+        ro.ids[a] = fr.ids[a];
+        ro.w[a] = fr.w[a];
+        ro.sa[fr.slot[a]] = a;
+        ro.ap[a] = fr.slot[a];
+    }
+    for (int e = tid; e <= E; e += 256) {
+        int below = 0, eq = 0;
+        for (int a = 0; a < n; a++) {
+            below += fr.ids[a] < e;
+            eq += fr.ids[a] == e;
+        }
+        ro.offsets[e] = below;
+        if (e < E) ro.counts[e] = eq;
+    }
+    for (int u = tid; u < fr.nT; u += 256) {
+        p.touched[u] = fr.touched[u];
+        p.tbase[u] = fr.tbase[u];
+        p.tcount[u] = fr.tcount[u];
+    }
+    if (tid == 0) p.meta[0] = fr.nT;
 }
 
-// ------------------------------------------------------------------ pass 1: gate / up
-template <int FMT>
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(int H, int I, int E, int k, WSet w,
+template <int FMT, int NMT, bool FUSED>
+__global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, int E, int k, int S,
+                                                          int renorm, WSet w,
                                                           const uint16_t *__restrict__ x,
-                                                          const int32_t *__restrict__ sa,
-                                                          Plan p, float *__restrict__ h)
+                                                          const int32_t *__restrict__ sa_in,
+                                                          Plan p, RouteOut ro,
+                                                          uint16_t *__restrict__ h)
 {
-    __shared__ float red[4][2][2][64][4];
-    const int nrb = I / 16;
+    __shared__ float red[4][NMT][64][4];
+    const int nrb = I / 8;
     const int u = blockIdx.x / nrb, rb = blockIdx.x - u * nrb;
-    if (u >= p.meta[0]) return;
-    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
-    const bool sh = (e == E);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    const int nmt = (cnt + 15) >> 4;
-    const uint16_t *xr[2];
+    int e, base, cnt;
+    const uint16_t *xr[NMT];
+    if (FUSED) {
+        __shared__ FusedRoute fr;
+        fused_select(T, E, k, S, renorm, ro, p, fr);
+        if (u >= fr.nT) return;
+        e = fr.touched[u];
+        base = fr.tbase[u];
+        cnt = fr.tcount[u];
+        // token of slot base + i: the assignment whose slot it is
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-        int idx = min(mt * 16 + r, cnt - 1);
-        int tok = sh ? idx : sa[base + idx] / k;
-        xr[mt] = x + (size_t)tok * H;
+        for (int mt = 0; mt < NMT; mt++) {
+            const int idx = min(mt * 16 + r, cnt - 1);
+            int tok = idx;
+            if (e != E)
+                for (int a = 0; a < T * k; a++)
+                    if (fr.slot[a] == base + idx) tok = a / k;
+            xr[mt] = x + (size_t)tok * H;
+        }
+    } else {
+        if (u >= p.meta[0]) return;
+        e = p.touched[u];
+        base = p.tbase[u];
+        cnt = p.tcount[u];
+#pragma unroll
+        for (int mt = 0; mt < NMT; mt++) {
+            const int idx = min(mt * 16 + r, cnt - 1);
+            const int tok = (e == E) ? idx : sa_in[base + idx] / k;
+            xr[mt] = x + (size_t)tok * H;
+        }
     }
-    const int row = rb * 16 + r;
-    f32x4 ag[2] = {}, au[2] = {};
-    float tsg = 1.f, tsu = 1.f;
-    if (FMT == 0) {
-        const size_t mb = (size_t)I * H * 2;
-        const uint16_t *Wg = reinterpret_cast<const uint16_t *>(expert_base(w.gate, e, E, mb)) + (size_t)row * H;
-        const uint16_t *Wu = reinterpret_cast<const uint16_t *>(expert_base(w.up, e, E, mb)) + (size_t)row * H;
-        const int nch = H / 32;
-        constexpr int UNR = 8;
-        for (int c0 = wave; c0 < nch; c0 += 4 * UNR) {
-            u32x4 bg[UNR], bu[UNR], a0[UNR], a1[UNR];
+    const bool sh = (e == E);
+    (void)sh;
+    const int nmt = (cnt + 15) >> 4;
+    const int i0 = rb * 8;
+    const int row = i0 + (r & 7);           // gate row (lanes r < 8) or up row (r >= 8)
+    const WMat &wm = (r < 8) ? w.gate : w.up;
+    f32x4 acc[NMT];
 #pragma unroll
-            for (int i = 0; i < UNR; i++) {
-                int c = c0 + 4 * i;
-                if (c < nch) {
-                    int k0 = c * 32 + g * 8;
-                    bg[i] = ld16(Wg + k0);
-                    bu[i] = ld16(Wu + k0);
-                    a0[i] = ld16(xr[0] + k0);
-                    if (nmt > 1) a1[i] = ld16(xr[1] + k0);
+    for (int mt = 0; mt < NMT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (FMT == 0) {
+        const uint16_t *W = reinterpret_cast<const uint16_t *>(expert_base(wm, e, E, (size_t)I * H * 2)) +
+                            (size_t)row * H;
+        const int cpw = H / 128;              // 32-wide chunks per wave (a contiguous K quarter)
+        const int kq = wave * cpw * 32 + g * 8;
+        constexpr int NB = 16;
+        int c0 = 0;
+        for (; c0 + NB <= cpw; c0 += NB) {   // full batches: every load issued, no branches
+            u32x4 b[NB], a[NMT][NB];
+#pragma unroll
+            for (int i = 0; i < NB; i++) b[i] = ld16(W + kq + (c0 + i) * 32);
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++)
+                if (NMT == 1 || mt < nmt)
+#pragma unroll
+                    for (int i = 0; i < NB; i++) a[mt][i] = ld16(xr[mt] + kq + (c0 + i) * 32);
+#pragma unroll
+            for (int i = 0; i < NB; i++)
+#pragma unroll
+                for (int mt = 0; mt < NMT; mt++)
+                    if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i]), as_bf16x8(b[i]), acc[mt]);
+        }
+        for (; c0 < cpw; c0++) {               // tail
+            const u32x4 b = ld16(W + kq + c0 * 32);
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++)
+                if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(ld16(xr[mt] + kq + c0 * 32)), as_bf16x8(b), acc[mt]);
+        }
+    } else {
+        // NVFP4: per 128-wide super-chunk a lane takes 32 consecutive k of its row (16
+        // bytes of codes, 2 block scales); MFMA j consumes the lane's k + 8j .. k + 8j + 7.
+        const uint8_t *Q = expert_base(wm, e, E, (size_t)I * H / 2) + (size_t)row * (H / 2);
+        const uint8_t *SF = expert_sf(wm, e, E, (size_t)I * H / 16) + (size_t)row * (H / 16);
+        const int nsc = H / 128;
+        constexpr int NB = 4;
+        for (int s0 = wave; s0 < nsc; s0 += 4 * NB) {
+            u32x4 q[NB], a[NMT][NB][4];
+            uint32_t sb[NB];
+#pragma unroll
+            for (int i = 0; i < NB; i++) {
+                const int sc = s0 + 4 * i;
+                if (sc < nsc) {
+                    const int kb = sc * 128 + g * 32;
+                    q[i] = ld16(Q + kb / 2);
+                    sb[i] = *reinterpret_cast<const uint16_t *>(SF + kb / 16);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < UNR; i++) {
-                int c = c0 + 4 * i;
-                if (c < nch) {
-                    ag[0] = mfma16x16x32(as_bf16x8(a0[i]), as_bf16x8(bg[i]), ag[0]);
-                    au[0] = mfma16x16x32(as_bf16x8(a0[i]), as_bf16x8(bu[i]), au[0]);
-                    if (nmt > 1) {
-                        ag[1] = mfma16x16x32(as_bf16x8(a1[i]), as_bf16x8(bg[i]), ag[1]);
-                        au[1] = mfma16x16x32(as_bf16x8(a1[i]), as_bf16x8(bu[i]), au[1]);
+            for (int mt = 0; mt < NMT; mt++)
+                if (NMT == 1 || mt < nmt)
+#pragma unroll
+                    for (int i = 0; i < NB; i++) {
+                        const int sc = s0 + 4 * i;
+                        if (sc < nsc)
+#pragma unroll
+                            for (int j = 0; j < 4; j++) a[mt][i][j] = ld16(xr[mt] + sc * 128 + g * 32 + 8 * j);
+                    }
+#pragma unroll
+            for (int i = 0; i < NB; i++) {
+                const int sc = s0 + 4 * i;
+                if (sc < nsc) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        bf16x8 bv = as_bf16x8(dequant8(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
+#pragma unroll
+                        for (int mt = 0; mt < NMT; mt++)
+                            if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, acc[mt]);
                     }
                 }
             }
         }
-    } else {
-        // NVFP4: a lane takes 32 consecutive k (16 bytes of codes, 2 block scales) of its
-        // row per 128-wide super-chunk; MFMA j consumes the lane's k + 8j .. k + 8j + 7.
-        const size_t mb = (size_t)I * H / 2, sb = (size_t)I * H / 16;
-        const uint8_t *Qg = expert_base(w.gate, e, E, mb) + (size_t)row * (H / 2);
-        const uint8_t *Qu = expert_base(w.up, e, E, mb) + (size_t)row * (H / 2);
-        const uint8_t *Sg = expert_sf(w.gate, e, E, sb) + (size_t)row * (H / 16);
-        const uint8_t *Su = expert_sf(w.up, e, E, sb) + (size_t)row * (H / 16);
-        tsg = expert_ts(w.gate, e, E);
-        tsu = expert_ts(w.up, e, E);
-        const int nsc = H / 128;
-        for (int sc = wave; sc < nsc; sc += 4) {
-            const int kb = sc * 128 + g * 32;
-            u32x4 qg = ld16(Qg + kb / 2), qu = ld16(Qu + kb / 2);
-            uint32_t sgb = *reinterpret_cast<const uint16_t *>(Sg + kb / 16);
-            uint32_t sub = *reinterpret_cast<const uint16_t *>(Su + kb / 16);
-            u32x4 a0[4], a1[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                a0[j] = ld16(xr[0] + kb + 8 * j);
-                if (nmt > 1) a1[j] = ld16(xr[1] + kb + 8 * j);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                float sgf = e4m3_to_f32((sgb >> (8 * (j >> 1))) & 0xffu);
-                float suf = e4m3_to_f32((sub >> (8 * (j >> 1))) & 0xffu);
-                bf16x8 bg = as_bf16x8(dequant8(qg[j], sgf));
-                bf16x8 bu = as_bf16x8(dequant8(qu[j], suf));
-                ag[0] = mfma16x16x32(as_bf16x8(a0[j]), bg, ag[0]);
-                au[0] = mfma16x16x32(as_bf16x8(a0[j]), bu, au[0]);
-                if (nmt > 1) {
-                    ag[1] = mfma16x16x32(as_bf16x8(a1[j]), bg, ag[1]);
-                    au[1] = mfma16x16x32(as_bf16x8(a1[j]), bu, au[1]);
-                }
-            }
-        }
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < NMT; mt++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            red[wave][mt][0][lane][i] = ag[mt][i];
-            red[wave][mt][1][lane][i] = au[mt][i];
-        }
+        for (int i = 0; i < 4; i++) red[wave][mt][lane][i] = acc[mt][i];
     __syncthreads();
-    for (int j = tid; j < nmt * 256; j += 256) {
-        const int mt = j >> 8, rem = j & 255, l = rem >> 2, i = rem & 3;
+    float tsg = 1.f, tsu = 1.f;
+    if (FMT == 1) {
+        tsg = expert_ts(w.gate, e, E);
+        tsu = expert_ts(w.up, e, E);
+    }
+    // D[m][n] sits in lane 16 (m / 4) + n, element m % 4; g in columns 0-7, u in 8-15.
+    for (int j = tid; j < nmt * 128; j += 256) {
+        const int mt = j >> 7, m = (j >> 3) & 15, i = j & 7;
+        const int lg = 16 * (m >> 2) + i, el = m & 3;
         float gs = 0.f, us = 0.f;
 #pragma unroll
         for (int wv = 0; wv < 4; wv++) {
-            gs += red[wv][mt][0][l][i];
-            us += red[wv][mt][1][l][i];
+            gs += red[wv][mt][lg][el];
+            us += red[wv][mt][lg + 8][el];
         }
-        const int m = 4 * (l >> 4) + i, n = l & 15;
         const int ti = mt * 16 + m;
-        if (ti < cnt) h[(size_t)(base + ti) * I + rb * 16 + n] = silu(gs * tsg) * (us * tsu);
+        if (ti < cnt) h[(size_t)(base + ti) * I + i0 + i] = (uint16_t)f2bf(silu(gs * tsg) * (us * tsu));
     }
 }
 
 // ------------------------------------------------------------------ pass 2: down + combine
-template <int FMT>
-__global__ __launch_bounds__(128) void gemv_down_kernel(int T, int H, int I, int E, int k, int S,
-                                                        WSet w, const float *__restrict__ h,
+template <int FMT, int NMT>
+__global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int E, int k, int S,
+                                                        WSet w, const uint16_t *__restrict__ h,
                                                         const float *__restrict__ topk_w,
                                                         const int32_t *__restrict__ ap, Plan p,
-                                                        float *__restrict__ o32,
                                                         uint16_t *__restrict__ y)
 {
-    __shared__ float red[2][2][64][4];
-    __shared__ int last;
-    const int nrb = H / 16;
-    const int u = blockIdx.x / nrb, rb = blockIdx.x - u * nrb;
+    __shared__ float o_lds[kGemvMaxT * 8 + kGemvMaxT][16];
+    const int n0 = blockIdx.x * 16;
     const int nT = p.meta[0];
-    if (u >= nT) return;
-    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    const int nmt = (cnt + 15) >> 4;
-    const float *hr[2];
+    const int row = n0 + r;
+    for (int u = wave; u < nT; u += 8) {
+        const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+        const int nmt = (cnt + 15) >> 4;
+        const uint16_t *hr[NMT];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) hr[mt] = h + (size_t)(base + min(mt * 16 + r, cnt - 1)) * I;
-    const int row = rb * 16 + r;
-    f32x4 acc[2] = {};
-    float ts = 1.f;
-    if (FMT == 0) {
-        const size_t mb = (size_t)H * I * 2;
-        const uint16_t *Wd = reinterpret_cast<const uint16_t *>(expert_base(w.down, e, E, mb)) + (size_t)row * I;
-        const int nch = I / 32;
-        constexpr int UNR = 6;
-        for (int c0 = wave; c0 < nch; c0 += 2 * UNR) {
-            u32x4 b[UNR];
+        for (int mt = 0; mt < NMT; mt++) hr[mt] = h + (size_t)(base + min(mt * 16 + r, cnt - 1)) * I;
+        f32x4 acc[NMT];
 #pragma unroll
-            for (int i = 0; i < UNR; i++) {
-                int c = c0 + 2 * i;
-                if (c < nch) b[i] = ld16(Wd + c * 32 + g * 8);
+        for (int mt = 0; mt < NMT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float ts = 1.f;
+        if (FMT == 0) {
+            const uint16_t *Wd = reinterpret_cast<const uint16_t *>(expert_base(w.down, e, E, (size_t)H * I * 2)) +
+                                 (size_t)row * I;
+            const int nch = I / 32;
+            constexpr int NB = NMT == 1 ? 24 : 12;
+            int c0 = 0;
+            for (; c0 + NB <= nch; c0 += NB) {   // full batches: every load issued, no branches
+                u32x4 b[NB], a[NMT][NB];
+#pragma unroll
+                for (int i = 0; i < NB; i++) b[i] = ld16(Wd + (c0 + i) * 32 + g * 8);
+#pragma unroll
+                for (int mt = 0; mt < NMT; mt++)
+                    if (NMT == 1 || mt < nmt)
+#pragma unroll
+                        for (int i = 0; i < NB; i++) a[mt][i] = ld16(hr[mt] + (c0 + i) * 32 + g * 8);
+#pragma unroll
+                for (int i = 0; i < NB; i++)
+#pragma unroll
+                    for (int mt = 0; mt < NMT; mt++)
+                        if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i]), as_bf16x8(b[i]), acc[mt]);
             }
+            for (; c0 < nch; c0++) {               // tail
+                const u32x4 b = ld16(Wd + c0 * 32 + g * 8);
 #pragma unroll
-            for (int i = 0; i < UNR; i++) {
-                int c = c0 + 2 * i;
-                if (c < nch) {
+                for (int mt = 0; mt < NMT; mt++)
+                    if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(ld16(hr[mt] + c0 * 32 + g * 8)), as_bf16x8(b), acc[mt]);
+            }
+        } else {
+            const uint8_t *Qd = expert_base(w.down, e, E, (size_t)H * I / 2) + (size_t)row * (I / 2);
+            const uint8_t *Sd = expert_sf(w.down, e, E, (size_t)H * I / 16) + (size_t)row * (I / 16);
+            ts = expert_ts(w.down, e, E);
+            const int nsc = I / 128;
+            constexpr int NB = NMT == 1 ? 6 : 3;
+            for (int s0 = 0; s0 < nsc; s0 += NB) {
+                u32x4 q[NB], a[NMT][NB][4];
+                uint32_t sb[NB];
 #pragma unroll
-                    for (int mt = 0; mt < 2; mt++) {
-                        if (mt < nmt) {
-                            const float *hv = hr[mt] + c * 32 + g * 8;
-                            float v[8];
-                            *reinterpret_cast<float4 *>(v) = *reinterpret_cast<const float4 *>(hv);
-                            *reinterpret_cast<float4 *>(v + 4) = *reinterpret_cast<const float4 *>(hv + 4);
-                            u32x4 hi, lo;
-                            split_bf16x8(v, hi, lo);
-                            acc[mt] = mfma16x16x32(as_bf16x8(hi), as_bf16x8(b[i]), acc[mt]);
-                            acc[mt] = mfma16x16x32(as_bf16x8(lo), as_bf16x8(b[i]), acc[mt]);
+                for (int i = 0; i < NB; i++) {
+                    if (s0 + i < nsc) {
+                        const int kb = (s0 + i) * 128 + g * 32;
+                        q[i] = ld16(Qd + kb / 2);
+                        sb[i] = *reinterpret_cast<const uint16_t *>(Sd + kb / 16);
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < NMT; mt++)
+                    if (NMT == 1 || mt < nmt)
+#pragma unroll
+                        for (int i = 0; i < NB; i++)
+                            if (s0 + i < nsc)
+#pragma unroll
+                                for (int j = 0; j < 4; j++) a[mt][i][j] = ld16(hr[mt] + (s0 + i) * 128 + g * 32 + 8 * j);
+#pragma unroll
+                for (int i = 0; i < NB; i++) {
+                    if (s0 + i < nsc) {
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            bf16x8 bv = as_bf16x8(dequant8(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
+#pragma unroll
+                            for (int mt = 0; mt < NMT; mt++)
+                                if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, acc[mt]);
                         }
                     }
                 }
             }
         }
-    } else {
-        const size_t mb = (size_t)H * I / 2, sb = (size_t)H * I / 16;
-        const uint8_t *Qd = expert_base(w.down, e, E, mb) + (size_t)row * (I / 2);
-        const uint8_t *Sd = expert_sf(w.down, e, E, sb) + (size_t)row * (I / 16);
-        ts = expert_ts(w.down, e, E);
-        const int nsc = I / 128;
-        for (int sc = wave; sc < nsc; sc += 2) {
-            const int kb = sc * 128 + g * 32;
-            u32x4 q = ld16(Qd + kb / 2);
-            uint32_t sbits = *reinterpret_cast<const uint16_t *>(Sd + kb / 16);
+        // D[m][n]: lane 16 (m / 4) + n, element m % 4; rows of this lane: m = 4 g + i.
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                bf16x8 b = as_bf16x8(dequant8(q[j], e4m3_to_f32((sbits >> (8 * (j >> 1))) & 0xffu)));
+        for (int mt = 0; mt < NMT; mt++)
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++) {
-                    if (mt < nmt) {
-                        const float *hv = hr[mt] + kb + 8 * j;
-                        float v[8];
-                        *reinterpret_cast<float4 *>(v) = *reinterpret_cast<const float4 *>(hv);
-                        *reinterpret_cast<float4 *>(v + 4) = *reinterpret_cast<const float4 *>(hv + 4);
-                        u32x4 hi, lo;
-                        split_bf16x8(v, hi, lo);
-                        acc[mt] = mfma16x16x32(as_bf16x8(hi), b, acc[mt]);
-                        acc[mt] = mfma16x16x32(as_bf16x8(lo), b, acc[mt]);
-                    }
-                }
+            for (int i = 0; i < 4; i++) {
+                const int ti = mt * 16 + 4 * g + i;
+                if ((NMT == 1 || mt < nmt) && ti < cnt) o_lds[base + ti][r] = acc[mt][i] * ts;
             }
-        }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) red[wave][mt][lane][i] = acc[mt][i];
-    __syncthreads();
-    for (int j = tid; j < nmt * 256; j += 128) {
-        const int mt = j >> 8, rem = j & 255, l = rem >> 2, i = rem & 3;
-        const float v = (red[0][mt][l][i] + red[1][mt][l][i]) * ts;
-        const int m = 4 * (l >> 4) + i, n = l & 15;
-        const int ti = mt * 16 + m;
-        if (ti < cnt) o32[(size_t)(base + ti) * H + rb * 16 + n] = v;
-    }
-    // Completion count for this 16-row block of H; the last workgroup combines it.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        int old = __hip_atomic_fetch_add(&p.counters[rb], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        last = (old == nT - 1);
     }
     __syncthreads();
-    if (!last) return;
-    __threadfence();
     const int TK = T * k;
-    for (int j = tid; j < T * 16; j += 128) {
-        const int t = j >> 4, n = rb * 16 + (j & 15);
-        float acc_y = S ? __builtin_nontemporal_load(o32 + (size_t)(TK + t) * H + n) : 0.f;
-        for (int jj = 0; jj < k; jj++) {
-            const int slot = ap[t * k + jj];
-            acc_y += topk_w[t * k + jj] * __builtin_nontemporal_load(o32 + (size_t)slot * H + n);
-        }
-        y[(size_t)t * H + n] = (uint16_t)f2bf(acc_y);
+    for (int j = tid; j < T * 16; j += 512) {
+        const int t = j >> 4, n = j & 15;
+        float acc_y = S ? o_lds[TK + t][n] : 0.f;
+        for (int jj = 0; jj < k; jj++) acc_y += topk_w[t * k + jj] * o_lds[ap[t * k + jj]][n];
+        y[(size_t)t * H + n0 + n] = (uint16_t)f2bf(acc_y);
     }
-    if (tid == 0) p.counters[rb] = 0;
+}
+
+template <int NMT, bool FUSED>
+static void launch_pair(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
+                        const float *topk_w, const int32_t *sa, const int32_t *ap,
+                        const Plan &plan, uint16_t *h, uint16_t *y, const RouteOut &ro,
+                        hipStream_t st)
+{
+    const int maxU = (int)std::min<int64_t>(T * s.k, s.E) + s.S;
+    const unsigned g1 = (unsigned)(maxU * (s.I / 8)), g2 = (unsigned)(s.H / 16);
+    if (w.fmt == 0) {
+        gemv_gateup_kernel<0, NMT, FUSED><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, s.renorm,
+                                                              w, x, sa, plan, ro, h);
+        gemv_down_kernel<0, NMT><<<g2, 512, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, w, h, topk_w, ap, plan, y);
+    } else {
+        gemv_gateup_kernel<1, NMT, FUSED><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, s.renorm,
+                                                              w, x, sa, plan, ro, h);
+        gemv_down_kernel<1, NMT><<<g2, 512, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, w, h, topk_w, ap, plan, y);
+    }
 }
 
 hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
-                               const Plan &plan, float *h, float *o32, uint16_t *y,
+                               const Plan &plan, uint16_t *h, uint16_t *y, const RouteOut *route,
                                hipStream_t st)
 {
-    const int maxU = (int)std::min<int64_t>(T * s.k, s.E) + s.S;
-    unsigned g1 = (unsigned)(maxU * (s.I / 16)), g2 = (unsigned)(maxU * (s.H / 16));
-    if (w.fmt == 0) {
-        gemv_gateup_kernel<0><<<g1, 256, 0, st>>>(s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        gemv_down_kernel<0><<<g2, 128, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, w, h, topk_w, ap,
-                                                 plan, o32, y);
-    } else {
-        gemv_gateup_kernel<1><<<g1, 256, 0, st>>>(s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        gemv_down_kernel<1><<<g2, 128, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, w, h, topk_w, ap,
-                                                 plan, o32, y);
-    }
+    const RouteOut ro = route ? *route : RouteOut{};
+    if (route && T <= kFusedSelectMaxT)
+        launch_pair<1, true>(s, w, T, x, route->w, route->sa, route->ap, plan, h, y, ro, st);
+    else if (T <= 16)
+        launch_pair<1, false>(s, w, T, x, topk_w, sa, ap, plan, h, y, ro, st);
+    else
+        launch_pair<2, false>(s, w, T, x, topk_w, sa, ap, plan, h, y, ro, st);
     return hipGetLastError();
 }
 

@@ -73,47 +73,45 @@ __device__ void build_plan(int T, int E, int k, int S, int H, const int *cnt, co
     for (int i = tid; i < H / 16; i += bd) p.counters[i] = 0;
 }
 
-// Single workgroup of 1024 threads.  Assignments are processed in chunks of 1024 in
-// ascending order; inside a chunk, a lane's rank among equal experts of lower lanes
-// comes from eight ballots over the expert id bits, and per-wave counts in LDS give
-// the offsets of earlier waves.  `cursor` carries each expert's fill level across
-// chunks, which makes the order stable.
-__global__ __launch_bounds__(1024) void permute_kernel(int T, int E, int k, int S, int H,
-                                                       const int32_t *__restrict__ ids,
-                                                       int32_t *__restrict__ counts,
-                                                       int32_t *__restrict__ offsets,
-                                                       int32_t *__restrict__ sa,
-                                                       int32_t *__restrict__ ap, Plan plan,
-                                                       int with_plan)
+// Grouping of n assignments by expert, by one workgroup of 1024 threads.  Assignments are
+// processed in chunks of 1024 in ascending order; inside a chunk, a lane's rank among
+// equal experts of lower lanes comes from eight ballots over the expert id bits, and
+// per-wave counts in LDS give the offsets of earlier waves.  `cursor` carries each
+// expert's fill level across chunks, which makes the order stable.  Leaves counts and
+// exclusive offsets in cnt/off (LDS).
+struct GroupScratch {
+    int cnt[256];
+    int off[257];
+    int cursor[256];
+    int wave_cnt[16][256];
+};
+
+__device__ void group_by_expert(int n, int E, const int32_t *ids, GroupScratch &g,
+                                int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                int32_t *__restrict__ sa, int32_t *__restrict__ ap)
 {
-    __shared__ int cnt[256];
-    __shared__ int off[257];
-    __shared__ int cursor[256];
-    __shared__ int wave_cnt[16][256];
-    __shared__ PlanScratch ps;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int n = T * k;
-    if (tid < 256) cnt[tid] = 0;
+    if (tid < 256) g.cnt[tid] = 0;
     __syncthreads();
     for (int a = tid; a < n; a += 1024) {
         int e = ids[a];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        if (e >= 0 && e < E) atomicAdd(&g.cnt[e], 1);
     }
     __syncthreads();
-    if (tid < 64) wave0_exclusive_scan(cnt, off, E);
+    if (tid < 64) wave0_exclusive_scan(g.cnt, g.off, E);
     __syncthreads();
     for (int e = tid; e < E; e += 1024) {
-        counts[e] = cnt[e];
-        offsets[e] = off[e];
-        cursor[e] = off[e];
+        counts[e] = g.cnt[e];
+        offsets[e] = g.off[e];
+        g.cursor[e] = g.off[e];
     }
-    if (tid == 0) offsets[E] = off[E];
+    if (tid == 0) offsets[E] = g.off[E];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base = 0; base < n; base += 1024) {
         const int a = base + tid;
         int e = (a < n) ? ids[a] : -1;
         const bool valid = (e >= 0 && e < E);
-        for (int i = tid; i < 16 * 256; i += 1024) (&wave_cnt[0][0])[i] = 0;
+        for (int i = tid; i < 16 * 256; i += 1024) (&g.wave_cnt[0][0])[i] = 0;
         __syncthreads();
         uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -123,24 +121,69 @@ __global__ __launch_bounds__(1024) void permute_kernel(int T, int E, int k, int 
             peers &= bit ? vote : ~vote;
         }
         const int rank = __popcll(peers & lt_mask);
-        if (valid && rank == 0) wave_cnt[wv][e] = __popcll(peers);
+        if (valid && rank == 0) g.wave_cnt[wv][e] = __popcll(peers);
         __syncthreads();
         if (valid) {
             int before = 0;
-            for (int w = 0; w < wv; w++) before += wave_cnt[w][e];
-            int pos = cursor[e] + before + rank;
+            for (int w = 0; w < wv; w++) before += g.wave_cnt[w][e];
+            int pos = g.cursor[e] + before + rank;
             sa[pos] = a;
             ap[a] = pos;
         }
         __syncthreads();
         for (int x = tid; x < E; x += 1024) {
             int tot = 0;
-            for (int w = 0; w < 16; w++) tot += wave_cnt[w][x];
-            cursor[x] += tot;
+            for (int w = 0; w < 16; w++) tot += g.wave_cnt[w][x];
+            g.cursor[x] += tot;
         }
         __syncthreads();
     }
-    if (with_plan) build_plan(T, E, k, S, H, cnt, off, plan, ps);
+}
+
+__global__ __launch_bounds__(1024) void permute_kernel(int T, int E, int k, int S, int H,
+                                                       const int32_t *__restrict__ ids,
+                                                       int32_t *__restrict__ counts,
+                                                       int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ sa,
+                                                       int32_t *__restrict__ ap, Plan plan,
+                                                       int with_plan)
+{
+    __shared__ GroupScratch g;
+    __shared__ PlanScratch ps;
+    group_by_expert(T * k, E, ids, g, counts, offsets, sa, ap);
+    if (with_plan) build_plan(T, E, k, S, H, g.cnt, g.off, plan, ps);
+}
+
+// Small batches (T <= 32): top-k of every token (one wave per token), the grouping and
+// the plan in a single workgroup, so routing costs one launch after the router.
+__global__ __launch_bounds__(1024) void select_permute_kernel(
+    int T, int E, int k, int S, int H, int renorm, const float *__restrict__ logits,
+    int32_t *__restrict__ ids, float *__restrict__ wout, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sa, int32_t *__restrict__ ap, Plan plan)
+{
+    __shared__ GroupScratch g;
+    __shared__ PlanScratch ps;
+    __shared__ int32_t s_ids[kGemvMaxT * 8];
+    __shared__ float s_w[kGemvMaxT * 8];
+    const int wv = threadIdx.x >> 6;
+    for (int t = wv; t < T; t += 16)
+        topk_token(logits + (size_t)t * E, E, k, renorm, s_ids + t * k, s_w + t * k);
+    __syncthreads();
+    for (int a = threadIdx.x; a < T * k; a += 1024) {
+        ids[a] = s_ids[a];
+        wout[a] = s_w[a];
+    }
+    group_by_expert(T * k, E, s_ids, g, counts, offsets, sa, ap);
+    build_plan(T, E, k, S, H, g.cnt, g.off, plan, ps);
+}
+
+hipError_t launch_select_permute(const Shape &s, int64_t T, const float *logits, int32_t *ids,
+                                 float *w, int32_t *counts, int32_t *offsets, int32_t *sa,
+                                 int32_t *ap, const Plan &plan, hipStream_t st)
+{
+    select_permute_kernel<<<1, 1024, 0, st>>>((int)T, s.E, s.k, s.S, s.H, s.renorm, logits, ids,
+                                              w, counts, offsets, sa, ap, plan);
+    return hipGetLastError();
 }
 
 hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t *counts,

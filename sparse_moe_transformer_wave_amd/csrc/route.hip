@@ -9,9 +9,9 @@
 namespace flint {
 
 // ---------------------------------------------------------------- decode router (T <= 32)
-// One wave per expert row: the 8 KB fp32 row is read once with 16-byte loads and dotted
-// against every token (x is tiny and stays in L2).  256 single-wave workgroups cover
-// E = 256, so the 2 MB of router weights stream from all CUs at once.
+// One wave per expert row: the fp32 row is read once (all 16-byte loads of a 2 KB slice in
+// flight together) and dotted against every token (x is tiny and stays in L2).  E
+// single-wave workgroups stream the whole router matrix from all CUs at once.
 template <int MAXT>
 __global__ __launch_bounds__(64) void router_small_kernel(int T, int H, int E,
                                                           const uint16_t *__restrict__ x,
@@ -25,16 +25,29 @@ __global__ __launch_bounds__(64) void router_small_kernel(int T, int H, int E,
 #pragma unroll
     for (int t = 0; t < MAXT; t++) acc[t] = 0.f;
     const float4 *w4 = reinterpret_cast<const float4 *>(Wr + (size_t)e * H);
-    for (int c = lane; c < H / 4; c += 64) {
-        float4 w = w4[c];
+    constexpr int NB = 8;  // float4 loads per lane per batch (a 2048-wide slice)
+    for (int c0 = 0; c0 < H / 4; c0 += 64 * NB) {
+        float4 w[NB];
+#pragma unroll
+        for (int i = 0; i < NB; i++) {
+            const int c = c0 + 64 * i + lane;
+            w[i] = c < H / 4 ? w4[c] : float4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int t = 0; t < MAXT; t++) {
             if (t < T) {
-                u32x2 xv = *reinterpret_cast<const u32x2 *>(x + (size_t)t * H + 4 * c);
-                acc[t] += bf2f(xv[0] & 0xffffu) * w.x;
-                acc[t] += bf2f(xv[0] >> 16) * w.y;
-                acc[t] += bf2f(xv[1] & 0xffffu) * w.z;
-                acc[t] += bf2f(xv[1] >> 16) * w.w;
+                const uint16_t *xt = x + (size_t)t * H;
+#pragma unroll
+                for (int i = 0; i < NB; i++) {
+                    const int c = c0 + 64 * i + lane;
+                    if (c < H / 4) {
+                        u32x2 xv = *reinterpret_cast<const u32x2 *>(xt + 4 * c);
+                        acc[t] += bf2f(xv[0] & 0xffffu) * w[i].x;
+                        acc[t] += bf2f(xv[0] >> 16) * w[i].y;
+                        acc[t] += bf2f(xv[1] & 0xffffu) * w[i].z;
+                        acc[t] += bf2f(xv[1] >> 16) * w[i].w;
+                    }
+                }
             }
         }
     }
@@ -114,28 +127,6 @@ hipError_t launch_router(const Shape &s, int64_t T, const uint16_t *x, const flo
 }
 
 // ---------------------------------------------------------------- top-k select
-// Order-preserving 64-bit key: high word = monotone image of the fp32 logit (-0 mapped to
-// +0, NaN below -inf), low word = 0xffff - e so that equal logits prefer the lower index.
-__device__ __forceinline__ uint64_t select_key(float v, int e)
-{
-    uint32_t u = __float_as_uint(v);
-    uint32_t ord;
-    if ((u & 0x7fffffffu) > 0x7f800000u) ord = 0u;           // NaN: below everything
-    else if (u == 0x80000000u) ord = 0x80000000u;              // -0 == +0
-    else ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(0xffffu - (uint32_t)e);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 // One wave per token; each lane holds experts lane, lane+64, lane+128, lane+192.
 // k rounds of a wave-wide arg-max; the winning lane retires its entry.
 __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k, int renorm,
@@ -143,43 +134,9 @@ __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k, int reno
                                                    int32_t *__restrict__ ids,
                                                    float *__restrict__ wout)
 {
-    const int lane = threadIdx.x % 64;
     const int t = blockIdx.x * 4 + threadIdx.x / 64;
     if (t >= T) return;
-    uint64_t key[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int e = lane + 64 * i;
-        key[i] = (e < E) ? select_key(logits[(size_t)t * E + e], e) : 0ull;
-    }
-    float sel_val[8];
-    int sel_id[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        if (j >= k) break;
-        uint64_t m = key[0];
-#pragma unroll
-        for (int i = 1; i < 4; i++) m = key[i] > m ? key[i] : m;
-        uint64_t best = wave_max_u64(m);
-        int e = (int)(0xffffu - (uint32_t)(best & 0xffffu));
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            if (key[i] == best) key[i] = 0ull;
-        sel_id[j] = e;
-        sel_val[j] = logits[(size_t)t * E + e];
-    }
-    if (lane == 0) {
-        float sg[8];
-        float sum = 0.f;
-        for (int j = 0; j < k; j++) {
-            sg[j] = 1.0f / (1.0f + expf(-sel_val[j]));
-            sum += sg[j];
-        }
-        for (int j = 0; j < k; j++) {
-            ids[(size_t)t * k + j] = sel_id[j];
-            wout[(size_t)t * k + j] = renorm ? sg[j] / sum : sg[j];
-        }
-    }
+    topk_token(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wout + (size_t)t * k);
 }
 
 hipError_t launch_topk(const Shape &s, int64_t T, const float *logits, int32_t *ids, float *w,
