@@ -22,7 +22,7 @@
  *     Nothing throws across the ABI.
  *   - T == 0 is a no-op returning FLINT_OK once the descriptor is valid.
  *   - Supported shapes: 1 <= E <= 256; 1 <= k <= min(8, E); n_shared in {0, 1};
- *     hidden % 128 == 0 and 128 <= hidden <= 8192; inter % 128 == 0 and
+ *     hidden % 256 == 0 and 256 <= hidden <= 8192; inter % 128 == 0 and
  *     128 <= inter <= 4096; 0 <= T <= 65536.  Every pointer must be 16-byte aligned.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
  */

@@ -25,7 +25,7 @@ int check_desc(const flint_moe_desc *d)
     if (d->n_experts < 1 || d->n_experts > 256) return FLINT_ERR_SHAPE;
     if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts) return FLINT_ERR_SHAPE;
     if (d->n_shared != 0 && d->n_shared != 1) return FLINT_ERR_SHAPE;
-    if (d->hidden < 128 || d->hidden > 8192 || d->hidden % 128) return FLINT_ERR_SHAPE;
+    if (d->hidden < 256 || d->hidden > 8192 || d->hidden % 256) return FLINT_ERR_SHAPE;
     if (d->inter < 128 || d->inter > 4096 || d->inter % 128) return FLINT_ERR_SHAPE;
     if (d->renormalize != 0 && d->renormalize != 1) return FLINT_ERR_SHAPE;
     return FLINT_OK;
@@ -120,6 +120,7 @@ WsLayout ws_layout(const Shape &s, int64_t T)
     L.sa = take(TK * 4);
     L.ap = take(TK * 4);
     L.plan = take((size_t)(4 + 3 * (s.E + 1) + L.max_items + s.H / 16) * 4);
+    L.hist = take(((TK + 1023) / 1024) * (size_t)s.E * 4);
     L.h = take(slots * s.I * 4);
     L.o = take(slots * s.H * 4);
     L.total = off;
@@ -203,8 +204,6 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
                       int32_t *counts, int32_t *offsets, int32_t *sorted_assign,
                       int32_t *assign_pos, void *ws, size_t ws_bytes, void *stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     int rc = check_desc(desc);
     if (rc) return rc;
     if (T < 0 || T > kMaxT) return FLINT_ERR_SHAPE;
@@ -214,8 +213,11 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
     for (const void *p : ptrs)
         if (!aligned16(p)) return FLINT_ERR_ALIGN;
     const Shape s = shape_of(desc);
+    const WsLayout L = ws_layout(s, T);
+    int32_t *hist = nullptr;
+    if (ws && ws_bytes >= L.total) hist = (int32_t *)((char *)ws + L.hist);
     return hip_status(launch_permute(s, T, topk_ids, counts, offsets, sorted_assign, assign_pos,
-                                     nullptr, (hipStream_t)stream));
+                                     nullptr, hist, (hipStream_t)stream));
 }
 
 static int forward_impl(const Shape &s, const WSet &wset, int64_t T, const uint16_t *x,
@@ -307,7 +309,8 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     } else {
         rc = hip_status(launch_topk(s, T, lg, ids, tw, st));
         if (rc) return rc;
-        rc = hip_status(launch_permute(s, T, ids, cnt, off, sa, ap, &plan, st));
+        rc = hip_status(launch_permute(s, T, ids, cnt, off, sa, ap, &plan,
+                                       (int32_t *)(b + L.hist), st));
         if (rc) return rc;
     }
     return forward_impl(s, wset_of(weights), T, x, tw, sa, ap, y, ws, L, plan, st);

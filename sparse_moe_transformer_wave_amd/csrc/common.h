@@ -22,8 +22,8 @@ struct Shape {
 // Streaming (GEMV-like) path handles T up to this many tokens; larger T uses the
 // grouped GEMM.  Two 16-token MFMA row tiles cover it.
 constexpr int kGemvMaxT = 32;
-// Grouped GEMM tile: BM rows (tokens) x 128 B-rows x 64 K.
-constexpr int kGemmBM = 128;
+// Grouped GEMM tile: BM rows (tokens) x 256 B-rows x 64 K.
+constexpr int kGemmBM = 256;
 
 // One weight matrix kind (gate, up or down) of all experts.
 // Routed expert e (< E) lives at routed + e * mat_bytes; the shared expert at `shared`.
@@ -54,7 +54,7 @@ struct Plan {
 // Workspace carve-up (byte offsets from the workspace base), computed on the host.
 struct WsLayout {
     size_t logits, ids, w, counts, offsets, sa, ap;
-    size_t plan, h, o;
+    size_t plan, hist, h, o;
     size_t total;
     int max_items;
 };
@@ -66,9 +66,10 @@ hipError_t launch_router(const Shape &s, int64_t T, const uint16_t *x, const flo
                          const float *bias, float *logits, hipStream_t st);
 hipError_t launch_topk(const Shape &s, int64_t T, const float *logits, int32_t *ids, float *w,
                        hipStream_t st);
+// hist: ceil(T*k / 1024) * E ints of workspace for the multi-block grouping (T*k > 4096).
 hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *sa, int32_t *ap, const Plan *plan,
-                          hipStream_t st);
+                          int32_t *hist, hipStream_t st);
 hipError_t launch_plan(const Shape &s, int64_t T, const int32_t *offsets, const Plan &plan,
                        hipStream_t st);
 // T <= kGemvMaxT: top-k, grouping and plan in one workgroup.

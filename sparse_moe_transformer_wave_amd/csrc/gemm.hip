@@ -5,8 +5,8 @@
 // expert FFNs run on bf16 MFMA with fp32 accumulation, LDS-staged tiles and a register
 // prefetch of the next K step.
 //
-// Work items come from the device plan: one item = (touched expert, 128-row tile of its
-// slots).  Gate/up: A = the expert's tokens gathered from x, B = 32 gate rows and the same
+// Work items come from the device plan: one item = (touched expert, 256-row tile of its
+// slots), so an expert of up to 256 rows streams its weights once.  Gate/up: A = the expert's tokens gathered from x, B = 32 gate rows and the same
 // 32 up rows per wave column, epilogue h = bf16(silu(g) * u).  Down: A = h rows of the
 // expert's slots (contiguous), epilogue o = bf16(acc).  The combine then forms
 // y = o_shared + sum_j w_j o_j per token, in that fixed order.
@@ -16,23 +16,38 @@ namespace flint {
 
 namespace {
 
-constexpr int BM = kGemmBM;  // rows (slots) per tile
-constexpr int BN = 128;      // B rows per tile
+constexpr int BM = kGemmBM;  // rows (slots) per tile: a uniform expert fits in one tile
+constexpr int BN = 256;      // B rows per tile
 constexpr int BK = 64;       // K per stage
 constexpr int LDP = BK + 8;  // padded LDS row (bf16 elements): 144 bytes
+constexpr int NT = 1024;     // 16 waves: 4 (M) x 4 (N), 64 x 64 per wave
+constexpr int NP = BM * (BK / 8) / NT;  // 16-byte chunks of A (and of B) staged per thread
+constexpr int kXcds = 8;     // workgroup b runs on XCD b % 8
 
 __device__ __forceinline__ u32x4 ld16g(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Workgroup b -> (item, N-tile): all N-tiles of an item go to one XCD, back to back, so
+// the item's A tile is fetched into that XCD's L2 once and reused.
+__device__ __forceinline__ void xcd_map(int b, int n_tiles, int &item, int &nb)
+{
+    const int x = b % kXcds, q = b / kXcds;
+    nb = q % n_tiles;
+    item = x + kXcds * (q / n_tiles);
+}
+
 template <int MODE, int FMT>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, int E, int k,
-                                                           WSet w,
-                                                           const uint16_t *__restrict__ asrc,
-                                                           const int32_t *__restrict__ sa,
-                                                           Plan p, uint16_t *__restrict__ out)
+__global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, int E, int k,
+                                                          WSet w,
+                                                          const uint16_t *__restrict__ asrc,
+                                                          const int32_t *__restrict__ sa,
+                                                          Plan p, uint16_t *__restrict__ out)
 {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
-    const int item = blockIdx.x;
+    const int N = MODE == 0 ? 2 * I : H;  // B rows of the whole problem
+    const int n_tiles = N / BN;
+    int item, nb;
+    xcd_map(blockIdx.x, n_tiles, item, nb);
     if (item >= p.meta[1]) return;
     const int code = p.items[item];
     const int u = code >> 16, mtile = code & 0xffff;
@@ -40,20 +55,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, 
     const bool sh = (e == E);
     const int m0 = mtile * BM;
     const int valid = min(BM, cnt - m0);
-    const int nb = blockIdx.y;
     const int K = MODE == 0 ? H : I;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
 
-    // Each thread stages 4 A rows and 4 B rows (one 16-byte chunk of each per stage).
-    const int srow = tid >> 3, schunk = tid & 7;
-    const uint16_t *arow[4];
-    const uint8_t *brow[4];
-    const uint8_t *bsf[4];
-    float bts[4];
+    // Staging: thread tid copies chunk tid + NT j (row = chunk / 8, 16-byte column chunk % 8).
+    const uint16_t *arow[NP];
+    const uint8_t *brow[NP];
+    const uint8_t *bsf[NP];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int rr = srow + 32 * j;
+    for (int j = 0; j < NP; j++) {
+        const int rr = (tid + NT * j) >> 3;
         const int ri = min(rr, valid - 1);
         if (MODE == 0) {
             const int tok = sh ? m0 + ri : sa[base + m0 + ri] / k;
@@ -61,13 +73,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, 
         } else {
             arow[j] = asrc + (size_t)(base + m0 + ri) * I;
         }
-        // B row rr of the tile
+        // B row rr of the tile.  Gate/up: each 64-row wave column holds 32 gate rows and the
+        // same 32 up rows, so g and u of one column meet in the same lane.
         const WMat *mat;
         int n;
         if (MODE == 0) {
             const int wcol = rr >> 6, within = rr & 63;
             mat = (within >> 5) ? &w.up : &w.gate;
-            n = nb * 64 + wcol * 32 + (within & 31);
+            n = nb * (BN / 2) + wcol * 32 + (within & 31);
         } else {
             mat = &w.down;
             n = nb * BN + rr;
@@ -76,20 +89,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, 
             const size_t mb = (size_t)H * I * 2;
             brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * K * 2;
             bsf[j] = nullptr;
-            bts[j] = 1.f;
         } else {
             const size_t mb = (size_t)H * I / 2, sb = (size_t)H * I / 16;
             brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2);
             bsf[j] = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * (K / 16);
-            bts[j] = sh ? *mat->ts_shared : mat->ts_routed[e];
         }
     }
-    (void)bts;
+    const int schunk = tid & 7;
 
-    u32x4 ra[4], rb[4];
+    u32x4 ra[NP], rb[NP];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < NP; j++) {
             ra[j] = ld16g(arow[j] + k0 + schunk * 8);
             if (FMT == 0) {
                 rb[j] = ld16g(brow[j] + (size_t)(k0 + schunk * 8) * 2);
@@ -103,9 +114,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, 
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            *reinterpret_cast<u32x4 *>(&As[buf][srow + 32 * j][schunk * 8]) = ra[j];
-            *reinterpret_cast<u32x4 *>(&Bs[buf][srow + 32 * j][schunk * 8]) = rb[j];
+        for (int j = 0; j < NP; j++) {
+            const int rr = (tid + NT * j) >> 3;
+            *reinterpret_cast<u32x4 *>(&As[buf][rr][schunk * 8]) = ra[j];
+            *reinterpret_cast<u32x4 *>(&Bs[buf][rr][schunk * 8]) = rb[j];
         }
     };
 
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, 
         const int buf = kt & 1;
         if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
+        for (int kk = 0; kk < BK / 32; kk++) {
             bf16x8 af[4], bfr[4];
 #pragma unroll
             for (int ms = 0; ms < 4; ms++)
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(int T, int H, int I, 
             if (MODE == 0) {
 #pragma unroll
                 for (int ns = 0; ns < 2; ns++) {
-                    const int col = nb * 64 + wn * 32 + ns * 16 + r;
+                    const int col = nb * (BN / 2) + wn * 32 + ns * 16 + r;
                     const float gv = acc[ms][ns][i] * tsg, uv = acc[ms][ns + 2][i] * tsu;
                     out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
                 }
@@ -219,14 +231,15 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
 {
     const int64_t slots = T * s.k + T * s.S;
     const int64_t max_items = (slots + kGemmBM - 1) / kGemmBM + s.E + s.S;
-    dim3 g1((unsigned)max_items, (unsigned)(s.I / 64));
-    dim3 g2((unsigned)max_items, (unsigned)(s.H / BN));
+    const int64_t item_slots = (max_items + kXcds - 1) / kXcds * kXcds;
+    const unsigned g1 = (unsigned)(item_slots * (2 * s.I / BN));
+    const unsigned g2 = (unsigned)(item_slots * (s.H / BN));
     if (w.fmt == 0) {
-        grouped_gemm_kernel<0, 0><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        grouped_gemm_kernel<1, 0><<<g2, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        grouped_gemm_kernel<0, 0><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        grouped_gemm_kernel<1, 0><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     } else {
-        grouped_gemm_kernel<0, 1><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        grouped_gemm_kernel<1, 1><<<g2, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        grouped_gemm_kernel<0, 1><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        grouped_gemm_kernel<1, 1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     }
     const int64_t nthreads = T * (s.H / 8);
     combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o,

@@ -186,13 +186,107 @@ hipError_t launch_select_permute(const Shape &s, int64_t T, const float *logits,
     return hipGetLastError();
 }
 
+// ---- many assignments (prefill): three launches instead of one serial workgroup ----
+// (1) per-block histograms of 1024 assignments, (2) one workgroup turns them into expert
+// offsets and per-(block, expert) bases, (3) each block places its assignments: base of
+// its (block, expert) + rank among equal experts of lower lanes in the block.  Blocks
+// are ordered like the assignments, so the grouping stays stable.
+__global__ __launch_bounds__(1024) void perm_hist_kernel(int n, int E, const int32_t *__restrict__ ids,
+                                                         int32_t *__restrict__ hist)
+{
+    __shared__ int cnt[256];
+    const int tid = threadIdx.x;
+    if (tid < 256) cnt[tid] = 0;
+    __syncthreads();
+    const int a = blockIdx.x * 1024 + tid;
+    if (a < n) {
+        const int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (tid < E) hist[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(256) void perm_scan_kernel(int T, int E, int k, int S, int H, int nb,
+                                                        int32_t *__restrict__ hist,
+                                                        int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets, Plan plan,
+                                                        int with_plan)
+{
+    __shared__ int cnt[256];
+    __shared__ int off[257];
+    __shared__ PlanScratch ps;
+    const int e = threadIdx.x;
+    int tot = 0;
+    if (e < E)
+        for (int b = 0; b < nb; b++) {
+            const int c = hist[(size_t)b * E + e];
+            hist[(size_t)b * E + e] = tot;  // exclusive prefix over blocks
+            tot += c;
+        }
+    if (e < 256) cnt[e] = (e < E) ? tot : 0;
+    __syncthreads();
+    if (threadIdx.x < 64) wave0_exclusive_scan(cnt, off, E);
+    __syncthreads();
+    if (e < E) {
+        counts[e] = cnt[e];
+        offsets[e] = off[e];
+        for (int b = 0; b < nb; b++) hist[(size_t)b * E + e] += off[e];
+    }
+    if (e == 0) offsets[E] = off[E];
+    if (with_plan) build_plan(T, E, k, S, H, cnt, off, plan, ps);
+}
+
+__global__ __launch_bounds__(1024) void perm_scatter_kernel(int n, int E, const int32_t *__restrict__ ids,
+                                                            const int32_t *__restrict__ base,
+                                                            int32_t *__restrict__ sa,
+                                                            int32_t *__restrict__ ap)
+{
+    __shared__ int wave_cnt[16][256];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int a = blockIdx.x * 1024 + tid;
+    const int e = (a < n) ? ids[a] : -1;
+    const bool valid = (e >= 0 && e < E);
+    for (int i = tid; i < 16 * 256; i += 1024) (&wave_cnt[0][0])[i] = 0;
+    __syncthreads();
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t vote = __ballot(bit);
+        peers &= bit ? vote : ~vote;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & lt);
+    if (valid && rank == 0) wave_cnt[wv][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+        int before = 0;
+        for (int w = 0; w < wv; w++) before += wave_cnt[w][e];
+        const int pos = base[(size_t)blockIdx.x * E + e] + before + rank;
+        sa[pos] = a;
+        ap[a] = pos;
+    }
+}
+
+constexpr int kSingleBlockPermuteMax = 4096;
+
 hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *sa, int32_t *ap, const Plan *plan,
-                          hipStream_t st)
+                          int32_t *hist, hipStream_t st)
 {
     Plan p = plan ? *plan : Plan{};
-    permute_kernel<<<1, 1024, 0, st>>>((int)T, s.E, s.k, s.S, s.H, ids, counts, offsets, sa, ap,
-                                       p, plan ? 1 : 0);
+    const int n = (int)(T * s.k);
+    if (n <= kSingleBlockPermuteMax || hist == nullptr) {
+        permute_kernel<<<1, 1024, 0, st>>>((int)T, s.E, s.k, s.S, s.H, ids, counts, offsets, sa, ap,
+                                           p, plan ? 1 : 0);
+        return hipGetLastError();
+    }
+    const int nb = (n + 1023) / 1024;
+    perm_hist_kernel<<<nb, 1024, 0, st>>>(n, s.E, ids, hist);
+    perm_scan_kernel<<<1, 256, 0, st>>>((int)T, s.E, s.k, s.S, s.H, nb, hist, counts, offsets, p,
+                                        plan ? 1 : 0);
+    perm_scatter_kernel<<<nb, 1024, 0, st>>>(n, s.E, ids, hist, sa, ap);
     return hipGetLastError();
 }
 

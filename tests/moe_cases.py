@@ -158,10 +158,14 @@ def to_host(out, c):
 
 
 def logit_bound(c: Case):
+    """A-priori bound of an fp32 sum of n exact products plus the bias: 2 (n + 2) u sum|x w|.
+    The streaming path (T <= 32) sums n = H products; the batched path splits each fp32
+    weight into three exact bf16 parts and sums n = 3H exact products."""
     xa = np.abs(dg.bf16_bits_to_f32(c.x).astype(np.float64))
     sa = xa @ np.abs(c.Wr.astype(np.float64)).T
     b = 0.0 if c.bias is None else np.abs(c.bias.astype(np.float64))[None, :]
-    return 2.0 * (c.H + 2) * U * sa + 2.0 * U * b
+    n = c.H if c.T <= 32 else 3 * c.H
+    return 2.0 * (n + 2) * U * sa + 2.0 * U * b
 
 
 def check_routing(c: Case, g, report=None):
