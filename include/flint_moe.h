@@ -130,7 +130,9 @@ int flint_moe_route(const flint_moe_desc *desc, int64_t T, const uint16_t *x,
    counts[e] = #assignments of expert e; offsets = exclusive scan (offsets[E] = T*k);
    sorted_assign = assignments grouped by expert, ascending a inside a group;
    assign_pos[a] = position of a in sorted_assign.  Integer, bit-exact.
-   Ids outside [0, E) are a caller error: their assignments are dropped. */
+   Ids outside [0, E) are a caller error: their assignments are dropped.
+   ws may be NULL; given flint_moe_workspace_bytes(desc, T, ...) bytes, large T
+   (T*k > 4096) uses a faster multi-block grouping with the same result. */
 int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk_ids,
                       int32_t *counts, int32_t *offsets, int32_t *sorted_assign,
                       int32_t *assign_pos, void *ws, size_t ws_bytes, void *stream);
@@ -139,9 +141,9 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
      y[t] = bf16( o_shared(t) + sum_j topk_w[t][j] * o_{topk_ids[t][j]}(t) ),
      o_e(t) = down_e( silu(gate_e x_t) * (up_e x_t) ),
    summed in fp32 in that order (shared first, then j ascending), which makes y
-   deterministic.  The expert intermediate h is rounded to bf16 before `down` on the
-   grouped-GEMM path (T > 32), and each per-slot output o is rounded to bf16 there
-   before the combine; the streaming path (T <= 32) keeps both in fp32.
+   deterministic.  The expert intermediate h is rounded to bf16 before `down`; on the
+   grouped-GEMM path (T > 32) each per-slot output o is also rounded to bf16 before the
+   combine, while the streaming path (T <= 32) combines o in fp32.
    topk_ids/topk_w/offsets/sorted_assign/assign_pos are the outputs of route and
    permute for the same T.  y: bf16 [T][H]. */
 int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,

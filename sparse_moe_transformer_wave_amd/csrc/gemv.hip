@@ -40,7 +40,7 @@ __device__ __forceinline__ float expert_ts(const WMat &m, int e, int E)
 
 // ------------------------------------------------------------------ pass 1: gate / up
 // Top-k of the T <= 8 tokens (wave t takes tokens t, t + 4) and their grouping, in LDS.
-// Workgroup 0 also writes the routing tensors and the plan for the down pass.
+// The publishing workgroup also writes the routing tensors and the plan for the down pass.
 struct FusedRoute {
     int32_t ids[64];
     float w[64];
@@ -50,7 +50,7 @@ struct FusedRoute {
 };
 
 __device__ void fused_select(int T, int E, int k, int S, int renorm, const RouteOut &ro,
-                             const Plan &p, FusedRoute &fr)
+                             const Plan &p, FusedRoute &fr, bool publish)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     for (int t = wave; t < T; t += 4)
@@ -61,7 +61,7 @@ __device__ void fused_select(int T, int E, int k, int S, int renorm, const Route
         if (lane == 0) fr.nT = nT;
     }
     __syncthreads();
-    if (blockIdx.x != 0) return;
+    if (!publish) return;
     const int n = T * k;
     for (int a = tid; a < n; a += 256) {
         ro.ids[a] = fr.ids[a];
@@ -101,21 +101,32 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
     int e, base, cnt;
     const uint16_t *xr[NMT];
     if (FUSED) {
-        __shared__ FusedRoute fr;
-        fused_select(T, E, k, S, renorm, ro, p, fr);
-        if (u >= fr.nT) return;
-        e = fr.touched[u];
-        base = fr.tbase[u];
-        cnt = fr.tcount[u];
-        // token of slot base + i: the assignment whose slot it is
+        // Unit 0 is the shared expert (all T tokens): its workgroups need no routing and
+        // start streaming at once; routed units u >= S select first.  The first routed
+        // unit's first workgroup publishes the routing tensors.
+        if (S && u == 0) {
+            e = E;
+            base = T * k;
+            cnt = T;
 #pragma unroll
-        for (int mt = 0; mt < NMT; mt++) {
-            const int idx = min(mt * 16 + r, cnt - 1);
-            int tok = idx;
-            if (e != E)
+            for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)min(mt * 16 + r, cnt - 1) * H;
+        } else {
+            __shared__ FusedRoute fr;
+            fused_select(T, E, k, S, renorm, ro, p, fr, blockIdx.x == (unsigned)(S * nrb));
+            const int ur = u - S;
+            if (ur >= fr.nT - S) return;
+            e = fr.touched[ur];
+            base = fr.tbase[ur];
+            cnt = fr.tcount[ur];
+            // token of slot base + i: the assignment whose slot it is
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) {
+                const int idx = min(mt * 16 + r, cnt - 1);
+                int tok = idx;
                 for (int a = 0; a < T * k; a++)
                     if (fr.slot[a] == base + idx) tok = a / k;
-            xr[mt] = x + (size_t)tok * H;
+                xr[mt] = x + (size_t)tok * H;
+            }
         }
     } else {
         if (u >= p.meta[0]) return;
@@ -248,6 +259,16 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
     const int nT = p.meta[0];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int row = n0 + r;
+    // The combine inputs of this thread's (token, column), fetched before the weights.
+    const int ct = tid >> 4;
+    float cw[8];
+    int cslot[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+        const bool on = ct < T && jj < k;
+        cw[jj] = on ? topk_w[ct * k + jj] : 0.f;
+        cslot[jj] = on ? ap[ct * k + jj] : 0;
+    }
     for (int u = wave; u < nT; u += 8) {
         const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
         const int nmt = (cnt + 15) >> 4;
@@ -334,12 +355,13 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
             }
     }
     __syncthreads();
-    const int TK = T * k;
-    for (int j = tid; j < T * 16; j += 512) {
-        const int t = j >> 4, n = j & 15;
-        float acc_y = S ? o_lds[TK + t][n] : 0.f;
-        for (int jj = 0; jj < k; jj++) acc_y += topk_w[t * k + jj] * o_lds[ap[t * k + jj]][n];
-        y[(size_t)t * H + n0 + n] = (uint16_t)f2bf(acc_y);
+    if (ct < T) {  // T * 16 <= 512 threads: one (token, column) each
+        const int n = tid & 15;
+        float acc_y = S ? o_lds[T * k + ct][n] : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++)
+            if (jj < k) acc_y += cw[jj] * o_lds[cslot[jj]][n];
+        y[(size_t)ct * H + n0 + n] = (uint16_t)f2bf(acc_y);
     }
 }
 
