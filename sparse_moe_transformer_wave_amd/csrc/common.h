@@ -126,26 +126,25 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c)
     return (c & 0x80u) ? -v : v;
 }
 
-// One E2M1 nibble times a block scale, as bf16 bits.  The product of a 2-bit and a
-// 4-bit significand is exact in fp32 and in bf16, so truncating to bf16 is exact.
-__device__ __forceinline__ uint32_t e2m1_scaled_bf16(uint32_t nib, float scale)
-{
-    uint32_t mag = nib & 7u;
-    float v = (mag < 2u) ? 0.5f * (float)mag : __uint_as_float((mag << 22) + (126u << 23));
-    uint32_t b = __float_as_uint(v * scale) >> 16;
-    return b | ((nib & 8u) << 12);
-}
-
-// Eight E2M1 nibbles (one 32-bit word, low nibble first) x scale -> 8 bf16 (4 words).
+// Eight E2M1 nibbles (one 32-bit word, low nibble first) times a block scale, as 8 bf16
+// (4 words).  gfx950's FP4 conversion applies only the power-of-two part of its scale
+// operand, so it yields e2m1 * 2^floor(log2 scale) exactly; one fp32 multiply by the
+// remaining mantissa factor (1 + m/8 for an E4M3 scale) completes the product.  A 2-bit
+// times a 4-bit significand is exact in fp32 and in bf16, so keeping the upper halves
+// (v_perm_b32) is exact.  A zero scale gives zeros.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 dequant8(uint32_t q, float scale)
 {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t lo = e2m1_scaled_bf16((q >> (8 * i)) & 15u, scale);
-        uint32_t hi = e2m1_scaled_bf16((q >> (8 * i + 4)) & 15u, scale);
-        r[i] = lo | (hi << 16);
-    }
+    const float mant = __uint_as_float((__float_as_uint(scale) & 0x007fffffu) | 0x3f800000u);
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 3);
+    auto pack = [mant](f32x2 v) {
+        return __builtin_amdgcn_perm(__float_as_uint(v[1] * mant), __float_as_uint(v[0] * mant), 0x07060302u);
+    };
+    u32x4 r{pack(v0), pack(v1), pack(v2), pack(v3)};
+    if (scale == 0.f) r = u32x4{0u, 0u, 0u, 0u};
     return r;
 }
 
