@@ -206,7 +206,7 @@ def main():
     dg.device_normal_bf16(x, 1, T * H, 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     desc = fm.desc(H, I, E, TOPK, S, 1)
-    ws = torch.empty(fm.workspace_bytes(desc, T, fmt), dtype=torch.uint8, device="cuda")
+    ws = fm.workspace(desc, T, fmt)
     torch.cuda.synchronize()
     log("pool ready (%.1f GB of expert weights) in %.1f s"
         % (L * (E + S) * EXPERT_BYTES[fmt] / 1e9, time.time() - t0))
@@ -278,7 +278,8 @@ def main():
         achieved = bytes_per_call / (avg_call_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
-                "kernel": "flint_moe_layer (one layer: all kernels)",
+                "kernel": ("decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
+                           "flint_moe_layer (router + fused select/gate-up + down kernels)"),
                 "avg_launch_us": round(avg_call_ms * 1e3, 2),
                 "alg_bytes_per_launch": int(bytes_per_call)}
     else:
@@ -292,7 +293,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "MoE-layer tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed_ms / K, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if fmt == 0 else "nvfp4-w4a16 (bf16 MFMA, fp32 accumulate)",
+        "dtype": "bf16" if fmt == 0 else "nvfp4-w4a16 (e2m1 weights x bf16 activations, fp32 accumulate)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tokens, drawn on device)",
         "config": {"workload": "%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, "
                                "SwiGLU, %s, %d distinct layers cycled%s"

@@ -25,6 +25,9 @@
  *     hidden % 256 == 0 and 256 <= hidden <= 8192; inter % 128 == 0 and
  *     128 <= inter <= 4096; 0 <= T <= 65536.  Every pointer must be 16-byte aligned.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
+ *   - A workspace's first 80 KiB hold the single-token path's launch counter, error flag
+ *     and exchange words: zero them once before first use (flint_moe_workspace_init, or
+ *     any zero fill) and leave them to the library afterwards.
  */
 #ifndef FLINT_MOE_H
 #define FLINT_MOE_H
@@ -109,6 +112,10 @@ typedef struct {
    given weight format.  Returns 0 for an invalid descriptor or T_max < 0. */
 size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int32_t format);
 
+/* Zero the first 80 KiB of a workspace (a small fill kernel on `stream`; no
+   allocation).  Call once per workspace before its first use. */
+int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code; for FLINT_ERR_HIP it also names the last HIP error
    seen by this library (the text is per thread and stays valid until the next call). */
 const char *flint_moe_status_string(int status);
@@ -154,7 +161,12 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
 
 /* The whole layer: route (x, w_router, logit_bias), permute and forward, with the same
    results as the three calls above.  `routing` (may be NULL) receives the intermediate
-   routing tensors the caller asks for. */
+   routing tensors the caller asks for.  A single token (T == 1) runs as one persistent
+   launch of one workgroup per CU (on a device with at least 256 CUs) whose workgroups
+   exchange logits and h through tagged words at the start of the workspace (see
+   flint_moe_workspace_init); it keeps h and the per-slot outputs in fp32.  A wait there
+   that runs out (it cannot on a device with a CU per workgroup) sets the word at byte 4
+   of the workspace to 1. */
 int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
                     const uint16_t *x, const float *w_router, const float *logit_bias,
                     uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,

@@ -6,7 +6,7 @@ kernels behind the C ABI (include/flint_moe.h).  There is no fallback: if the na
 library is missing, every call raises.
 
 Entry points (same names as the C ABI, without the prefix):
-  workspace_bytes(desc, T_max, fmt)
+  workspace_bytes(desc, T_max, fmt), workspace_init(ws), workspace(desc, T_max, fmt)
   route(desc, x, w_router, bias, topk_ids, topk_w, ws, logits=None, logits_in=False)
   permute(desc, topk_ids, counts, offsets, sorted_assign, assign_pos, ws)
   forward(desc, weights, x, topk_ids, topk_w, offsets, sorted_assign, assign_pos, y, ws)
@@ -25,8 +25,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_FORMAT, ERR_HIP = range(7
 WFMT_BF16, WFMT_NVFP4 = 0, 1
 ROUTE_LOGITS_IN = 1
 
-EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_status_string", "flint_moe_route",
-            "flint_moe_permute", "flint_moe_forward", "flint_moe_layer")
+EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_workspace_init", "flint_moe_status_string",
+            "flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer")
 
 
 class FlintError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
         vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
         L.flint_moe_workspace_bytes.argtypes = [vp, i64, ctypes.c_int32]
         L.flint_moe_workspace_bytes.restype = sz
+        L.flint_moe_workspace_init.argtypes = [vp, sz, vp]
+        L.flint_moe_workspace_init.restype = ctypes.c_int
         L.flint_moe_status_string.argtypes = [ctypes.c_int]
         L.flint_moe_status_string.restype = ctypes.c_char_p
         L.flint_moe_route.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
@@ -143,6 +145,20 @@ class Weights:
 
 def workspace_bytes(d: Desc, T_max: int, fmt: int = WFMT_BF16) -> int:
     return int(lib().flint_moe_workspace_bytes(ctypes.byref(d), T_max, fmt))
+
+
+def workspace_init(ws, stream=None):
+    """Zero the synchronisation words of a workspace tensor (once, before first use)."""
+    _check(lib().flint_moe_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)),
+           "flint_moe_workspace_init")
+
+
+def workspace(d: Desc, T_max: int, fmt: int = WFMT_BF16):
+    """Allocate (torch, on the current device) and initialise a workspace for T <= T_max."""
+    import torch
+    ws = torch.empty(max(workspace_bytes(d, T_max, fmt), 1024), dtype=torch.uint8, device="cuda")
+    workspace_init(ws)
+    return ws
 
 
 def route(d: Desc, T: int, x, w_router, bias, topk_ids, topk_w, ws, logits=None,

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip", "decode1.hip"]
 
 
 def _run(cmd):

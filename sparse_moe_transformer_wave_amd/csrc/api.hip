@@ -112,6 +112,7 @@ WsLayout ws_layout(const Shape &s, int64_t T)
         off = align_up(off + bytes, 256);
         return o;
     };
+    L.sync = take(kSyncBytes);  // always at offset 0, whatever T
     L.logits = take((size_t)T * s.E * 4);
     L.ids = take(TK * 4);
     L.w = take(TK * 4);
@@ -140,9 +141,25 @@ Plan plan_view(void *ws, const WsLayout &L, const Shape &s)
     return p;
 }
 
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 }  // namespace flint
 
 extern "C" {
+
+int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ws) return FLINT_ERR_NULL;
+    if (!aligned16(ws)) return FLINT_ERR_ALIGN;
+    if (ws_bytes < kSyncBytes) return FLINT_ERR_WORKSPACE;
+    const int n = (int)(kSyncBytes / 4);
+    flint::zero_words_kernel<<<(n + 255) / 256, 256, 0, (hipStream_t)stream>>>((uint32_t *)ws, n);
+    return hip_status(hipGetLastError());
+}
 
 size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int32_t format)
 {
@@ -297,6 +314,10 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     int32_t *ap = R.assign_pos ? R.assign_pos : (int32_t *)(b + L.ap);
     hipStream_t st = (hipStream_t)stream;
     const Plan plan = plan_view(ws, L, s);
+    if (T == 1 && decode1_supported(s, weights->format)) {
+        return hip_status(launch_decode1(s, wset_of(weights), x, w_router, logit_bias, y, lg, ids, tw,
+                                         cnt, off, sa, ap, b + L.sync, st));
+    }
     rc = hip_status(launch_router(s, T, x, w_router, logit_bias, lg, st));
     if (rc) return rc;
     if (T <= kFusedSelectMaxT) {

@@ -54,7 +54,7 @@ struct Plan {
 // Workspace carve-up (byte offsets from the workspace base), computed on the host.
 struct WsLayout {
     size_t logits, ids, w, counts, offsets, sa, ap;
-    size_t plan, hist, h, o;
+    size_t sync, plan, hist, h, o;
     size_t total;
     int max_items;
 };
@@ -76,6 +76,16 @@ hipError_t launch_plan(const Shape &s, int64_t T, const int32_t *offsets, const 
 hipError_t launch_select_permute(const Shape &s, int64_t T, const float *logits, int32_t *ids,
                                  float *w, int32_t *counts, int32_t *offsets, int32_t *sa,
                                  int32_t *ap, const Plan &plan, hipStream_t st);
+// Single-token layer in one persistent launch (decode1.hip).  `head` = the workspace's
+// first kSyncBytes (launch counter and exchange words; zero before first use).
+// decode1_supported also checks that the current device has a CU for every workgroup.
+constexpr size_t kSyncBytes = 80 * 1024;
+bool decode1_supported(const Shape &s, int fmt);
+hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, const float *Wr,
+                          const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
+                          int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
+                          hipStream_t st);
+
 // Routing outputs a fused small-batch launch writes (workgroup 0) for later kernels.
 struct RouteOut {
     const float *logits;

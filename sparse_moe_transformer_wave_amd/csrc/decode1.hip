@@ -1,0 +1,539 @@
+// decode1.hip -- the whole MoE layer for one token in a single persistent launch.
+//
+// Decode of one token reads only the active weights (qantcore.space review, section 01),
+// 68 MB per layer at H=2048, I=768, so a layer is ~11 us of HBM streaming.  On this GPU
+// every kernel launch costs ~1.6 us and every dependent global round trip ~1.5-2 us, so
+// the layer runs as one launch of one workgroup per CU in three phases:
+//
+//   phase 1  router row e = workgroup id (fp32, one wave); the shared expert's gate/up rows
+//            of this workgroup's I-slice (known before routing: news.ditty.ir, third
+//            paragraph, one shared expert always active) -> h of the shared slot; the
+//            shared expert's down rows of this workgroup's H-slice go straight into LDS.
+//   wait     for the 256 logit words.
+//   phase 2  every wave selects the top-k of the 256 logits itself (same code, same bits,
+//            so every copy agrees).  Right after round j it issues its loads for slot j:
+//            its gate/up row of that expert (workgroup b owns rows [b I/256, (b+1) I/256)
+//            of every selected expert: the single token is the same for every expert) and
+//            its share of the expert's down rows of the H-slice, copied HBM -> LDS without
+//            registers.  The later selection rounds run while the first slots stream.
+//   wait     for the (k + 1) * I words of h.
+//   phase 3  down rows from LDS against h (bf16, as on every path), one slot per wave and
+//            8 lanes per row; combine (shared first, then j ascending) -> y.
+//
+// Cross-workgroup data (logits, h) moves as 64-bit exchange words {launch tag, fp32 value}
+// written with agent-scope stores and polled with agent-scope loads: one aligned 64-bit
+// access carries the value and its readiness together, so there are no grid barriers,
+// fences or cache-wide write-backs, and a reader waits one round trip after the word it
+// needs lands.  The tag is the launch counter at the start of the workspace plus one;
+// workgroup 0 advances the counter once it has seen every workgroup's phase-1 word (each
+// was written after its writer read the counter), and the next launch on the stream
+// starts after this one ends.  Every wait is bounded: on timeout the kernel sets an error
+// word and carries on.  All 256 workgroups must be resident together (one per CU); the
+// host checks the CU count before choosing this launch.
+#include "common.h"
+
+namespace flint {
+
+namespace {
+
+constexpr int kG = 256;        // workgroups (one per CU)
+constexpr int kWaves = 8;
+constexpr int kMaxK = 8;
+constexpr int kMaxXC = 4;      // 16-byte x chunks per lane: H <= 2048
+constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
+
+// Workspace words of this launch (the zero-initialised head of the workspace):
+// u32 [0] launch counter, u32 [1] error flag; u64 exchange words for the logits at byte
+// 1024 (one per workgroup) and for h at byte 3072 ([k + 1][I], slot k = shared expert).
+constexpr int kCtlEpoch = 0, kCtlError = 1;
+constexpr size_t kXLogOff = 1024, kXHOff = kXLogOff + 8 * kG;
+static_assert(kXHOff + 8 * (size_t)(kMaxK + 1) * 1024 <= kSyncBytes, "exchange words exceed the head");
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// 16 bytes per lane from HBM straight into LDS: lane l writes lds + 16 l (lds is uniform).
+__device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void put_word(uint64_t *p, uint32_t tag, float v)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_word(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until the words w[q] (q < nq, read from p + stride * q) all carry `tag`.  The
+// missing ones are re-read together, so each try costs one round trip however many are
+// late.  Bounded: on timeout the error flag is set and the stale values are kept.
+template <int N>
+__device__ __forceinline__ void await_words(const uint64_t *p, int stride, int nq, uint64_t *w, uint32_t tag,
+                                            uint32_t *ctl)
+{
+    for (int n = 0;; n++) {
+        bool miss = false;
+#pragma unroll
+        for (int q = 0; q < N; q++) miss |= q < nq && (uint32_t)(w[q] >> 32) != tag;
+        if (!miss) break;
+        if (n >= kSpin) {
+            __hip_atomic_store(ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int q = 0; q < N; q++)
+            if (q < nq && (uint32_t)(w[q] >> 32) != tag) w[q] = get_word(p + (size_t)stride * q);
+    }
+}
+
+// 8 bf16 products summed into acc.  The elements go through named scalars: a bit cast
+// taken directly of an indexed vector element in an unrolled loop reads element 0 every
+// time with this compiler.
+__device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 x, float acc)
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t wi = w[i], xi = x[i];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), __builtin_bit_cast(bf16x2, xi), acc, false);
+    }
+    return acc;
+}
+
+// One 16-byte NVFP4 chunk (32 codes = 2 blocks of 16) against 32 fp32 x values:
+// sum over each block of e2m1 * x, times the block's E4M3 scale.
+__device__ __forceinline__ float dot32_nvfp4(u32x4 q, uint32_t sb2, const float *xv)
+{
+    float blk[2] = {0.f, 0.f};
+#pragma unroll
+    for (int wd = 0; wd < 4; wd++) {
+        const uint32_t qw = q[wd];
+        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw, 1.0f, 0);
+        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw, 1.0f, 1);
+        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw, 1.0f, 2);
+        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw, 1.0f, 3);
+        const float *xp = xv + 8 * wd;
+        float s = blk[wd >> 1];
+        s += v0[0] * xp[0];
+        s += v0[1] * xp[1];
+        s += v1[0] * xp[2];
+        s += v1[1] * xp[3];
+        s += v2[0] * xp[4];
+        s += v2[1] * xp[5];
+        s += v3[0] * xp[6];
+        s += v3[1] * xp[7];
+        blk[wd >> 1] = s;
+    }
+    return blk[0] * e4m3_to_f32(sb2 & 0xffu) + blk[1] * e4m3_to_f32((sb2 >> 8) & 0xffu);
+}
+
+// Eight E2M1 codes (one word, low nibble first) against 8 bf16 h values: exact e2m1
+// values as bf16 pairs, then bf16 dot products.
+__device__ __forceinline__ float dot8_fp4_bf16(uint32_t q, u32x4 h, float acc)
+{
+    const uint32_t h0 = h[0], h1 = h[1], h2 = h[2], h3 = h[3];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0), __builtin_bit_cast(bf16x2, h0), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1), __builtin_bit_cast(bf16x2, h1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2), __builtin_bit_cast(bf16x2, h2), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3), __builtin_bit_cast(bf16x2, h3), acc, false);
+    return acc;
+}
+
+struct D1Args {
+    int H, I, E, k, S, renorm;
+    WSet w;
+    const uint16_t *x;
+    const float *Wr, *bias;
+    uint16_t *y;
+    float *logits;
+    int32_t *ids;
+    float *tw;
+    int32_t *counts, *offsets, *sa, *ap;
+    uint32_t *ctl;   // launch counter, error flag
+    uint64_t *xlog;  // [256] exchange words: logit of expert b (workgroup b)
+    uint64_t *xh;    // [k + S][I] exchange words: slot j < k = j-th selected expert, slot k = shared
+};
+
+__device__ __forceinline__ const uint8_t *mat_base(const WMat &m, int e, int E, size_t bytes)
+{
+    return e == E ? m.shared : m.routed + (size_t)e * bytes;
+}
+__device__ __forceinline__ const uint8_t *mat_sf(const WMat &m, int e, int E, size_t bytes)
+{
+    return e == E ? m.sf_shared : m.sf_routed + (size_t)e * bytes;
+}
+__device__ __forceinline__ float mat_ts(const WMat &m, int e, int E)
+{
+    return e == E ? *m.ts_shared : m.ts_routed[e];
+}
+
+// One gate or up row (expert e, row i) of a wave in flight: bf16 lane chunks lane + 64 c,
+// or the lane's NVFP4 chunk with its two block scales and the tensor scale.
+template <int FMT>
+struct RowLoad {
+    u32x4 v[FMT == 0 ? kMaxXC : 1];
+    uint32_t sb;
+    float ts;
+};
+
+template <int FMT>
+__device__ __forceinline__ void row_issue(const D1Args &a, const WMat &m, int e, int i, RowLoad<FMT> &r)
+{
+    const int lane = threadIdx.x & 63, H = a.H, I = a.I, E = a.E;
+    if (FMT == 0) {
+        const uint16_t *row = reinterpret_cast<const uint16_t *>(mat_base(m, e, E, (size_t)I * H * 2)) + (size_t)i * H;
+#pragma unroll
+        for (int c = 0; c < kMaxXC; c++)
+            if (lane + 64 * c < H / 8) r.v[c] = ld16(row + 8 * (lane + 64 * c));
+    } else {
+        const uint8_t *row = mat_base(m, e, E, (size_t)I * H / 2) + (size_t)i * (H / 2);
+        const uint8_t *sf = mat_sf(m, e, E, (size_t)I * H / 16) + (size_t)i * (H / 16);
+        if (lane < H / 32) {
+            r.v[0] = ld16(row + 16 * lane);
+            r.sb = *reinterpret_cast<const uint16_t *>(sf + 2 * lane);
+        }
+        r.ts = mat_ts(m, e, E);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ float row_dot(const D1Args &a, const RowLoad<FMT> &r, const u32x4 *xb, const float *xf)
+{
+    const int lane = threadIdx.x & 63, H = a.H;
+    float acc = 0.f;
+    if (FMT == 0) {
+#pragma unroll
+        for (int c = 0; c < kMaxXC; c++)
+            if (lane + 64 * c < H / 8) acc = dot8_bf16(r.v[c], xb[c], acc);
+        return wave_sum(acc);
+    }
+    if (lane < H / 32) acc = dot32_nvfp4(r.v[0], r.sb, xf);
+    return wave_sum(acc) * r.ts;
+}
+
+struct D1Shared {
+    float lg[kG];                 // the logits, for every wave's selection
+    float gs[4], us[4];           // shared expert gate / up of this workgroup's pairs
+    float g[kMaxK][4], u[kMaxK][4];
+    int32_t ids[kMaxK];
+    float wt[kMaxK];
+    float dts[kMaxK + 1];         // NVFP4 down tensor scale of every slot
+    float o[kMaxK + 1][8];        // per-slot down outputs of this workgroup's rows_h columns
+    __attribute__((aligned(16))) uint16_t hb[(kMaxK + 1) * 1024];  // h of every slot, bf16 [slot][I]
+};
+
+template <int FMT>
+__global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];  // down rows of this H-slice
+    __shared__ D1Shared sh;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int b = blockIdx.x;
+    const int H = a.H, I = a.I, E = a.E, k = a.k, S = a.S, ns = k + S;
+    const int rows_h = H / kG;                        // down rows (columns of y) per workgroup
+    const int n0 = b * rows_h;
+    const int i0 = b * I / kG, npair = (b + 1) * I / kG - i0;  // gate/up rows of every expert
+    const uint32_t tag = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const size_t drow_bytes = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2 + I / 16;
+    const int cpb = (int)(rows_h * drow_bytes / 16);  // 16-byte chunks per slot block
+    const int ngrp = (cpb + 63) / 64;                 // 64-chunk groups per slot block
+
+    // Token in registers: bf16 chunks for the bf16 dot, fp32 for the NVFP4 dot.
+    u32x4 xb[kMaxXC];
+    float xf[32];
+    if (FMT == 0) {
+#pragma unroll
+        for (int c = 0; c < kMaxXC; c++) xb[c] = (lane + 64 * c < H / 8) ? ld16(a.x + 8 * (lane + 64 * c)) : u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            u32x4 v = (lane < H / 32) ? ld16(a.x + 32 * lane + 8 * i) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t vj = v[j];
+                xf[8 * i + 2 * j] = bf2f(vj & 0xffffu);
+                xf[8 * i + 2 * j + 1] = bf2f(vj >> 16);
+            }
+        }
+    }
+
+    // Down rows of this H-slice, slot block j at dyn + j * cpb * 16: chunk c (16 bytes).
+    // For NVFP4 a block is the rows' codes followed by their block scales (each contiguous
+    // in HBM for a run of rows).  Wave w copies chunk groups w, w + 8, ...
+    auto load_down = [&](int j, int e) {
+        const int ncq = rows_h * I / 32;
+        for (int g = wave; g < ngrp; g += kWaves) {
+            const int c = 64 * g + lane;
+            if (c < cpb) {
+                const uint8_t *src;
+                if (FMT == 0) src = mat_base(a.w.down, e, E, (size_t)H * I * 2) + (size_t)n0 * I * 2 + 16 * c;
+                else if (c < ncq) src = mat_base(a.w.down, e, E, (size_t)H * I / 2) + (size_t)n0 * (I / 2) + 16 * c;
+                else src = mat_sf(a.w.down, e, E, (size_t)H * I / 16) + (size_t)n0 * (I / 16) + 16 * (c - ncq);
+                lds_load16(src, dyn + ((size_t)j * cpb + 64 * g) * 16);
+            }
+        }
+    };
+
+    // ---------------- phase 1
+    if (S) load_down(k, E);
+    if (wave == 0) {
+        const int e = b;  // E <= 256: workgroup b computes logit b, if there is one
+        if (e < E) {      // router row: one logit, all loads in flight
+            const float4 *w4 = reinterpret_cast<const float4 *>(a.Wr + (size_t)e * H);
+            float4 wv[8];
+            u32x2 xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int c = lane + 64 * i;
+                wv[i] = c < H / 4 ? w4[c] : float4{0.f, 0.f, 0.f, 0.f};
+                xv[i] = c < H / 4 ? *reinterpret_cast<const u32x2 *>(a.x + 4 * c) : u32x2{0u, 0u};
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t x0 = xv[i][0], x1 = xv[i][1];
+                acc += bf2f(x0 & 0xffffu) * wv[i].x;
+                acc += bf2f(x0 >> 16) * wv[i].y;
+                acc += bf2f(x1 & 0xffffu) * wv[i].z;
+                acc += bf2f(x1 >> 16) * wv[i].w;
+            }
+            const float l = wave_sum(acc) + (a.bias ? a.bias[e] : 0.f);
+            if (lane == 0) {
+                a.logits[e] = l;
+                put_word(a.xlog + b, tag, l);
+            }
+        } else if (lane == 0) {
+            put_word(a.xlog + b, tag, 0.f);  // no expert: the word only says "counter read"
+        }
+    } else if (S) {
+        // shared expert rows r = 2 (i - i0) + {0 gate, 1 up}, r < 2 npair: wave 1 + r % 7
+        RowLoad<FMT> r0, r1;
+        const int ra = wave - 1, rb = wave + 6;
+        if (ra < 2 * npair) row_issue<FMT>(a, (ra & 1) ? a.w.up : a.w.gate, E, i0 + (ra >> 1), r0);
+        if (rb < 2 * npair) row_issue<FMT>(a, (rb & 1) ? a.w.up : a.w.gate, E, i0 + (rb >> 1), r1);
+        if (ra < 2 * npair) {
+            const float v = row_dot<FMT>(a, r0, xb, xf);
+            if (lane == 0) ((ra & 1) ? sh.us : sh.gs)[ra >> 1] = v;
+        }
+        if (rb < 2 * npair) {
+            const float v = row_dot<FMT>(a, r1, xb, xf);
+            if (lane == 0) ((rb & 1) ? sh.us : sh.gs)[rb >> 1] = v;
+        }
+    }
+    __syncthreads();
+    if (S && tid < npair) put_word(a.xh + (size_t)k * I + i0 + tid, tag, silu(sh.gs[tid]) * sh.us[tid]);
+
+    // ---------------- phase 2: selection (every wave), routed gate/up rows, down rows
+    if (wave == 0) {
+        uint64_t lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) lw[i] = get_word(a.xlog + lane + 64 * i);
+        await_words<4>(a.xlog + lane, 64, 4, lw, tag, a.ctl);
+#pragma unroll
+        for (int i = 0; i < 4; i++) sh.lg[lane + 64 * i] = __uint_as_float((uint32_t)lw[i]);
+        // every workgroup has read the counter: the next launch may use the next tag
+        if (b == 0 && lane == 0) __hip_atomic_store(a.ctl + kCtlEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    // Lane holds experts lane + 64 i.  Key = order of the logit (select_key's high word)
+    // plus one, 0 = no expert or already taken, so a NaN logit (order 0) still ranks above
+    // those.  Each round takes the largest key; among equal keys the lowest expert, found
+    // as the first i with a match and the lowest lane in it.
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? (uint32_t)(select_key(sh.lg[e], e) >> 32) + 1u : 0u;
+    }
+    const bool has_row = wave < 2 * npair;  // this wave's row: pair i0 + wave / 2, gate if even
+    const WMat &my_mat = (wave & 1) ? a.w.up : a.w.gate;
+    int sel[kMaxK];
+    uint32_t ordv[kMaxK];
+    RowLoad<FMT> rl[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; j++) {
+        if (j < k) {
+            const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+            const uint64_t b0 = __ballot(key[0] == m), b1 = __ballot(key[1] == m);
+            const uint64_t b2 = __ballot(key[2] == m), b3 = __ballot(key[3] == m);
+            const int i = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
+            const int wl = __builtin_ctzll(b0 ? b0 : b1 ? b1 : b2 ? b2 : b3);
+            if (lane == wl) {
+                key[0] = i == 0 ? 0u : key[0];
+                key[1] = i == 1 ? 0u : key[1];
+                key[2] = i == 2 ? 0u : key[2];
+                key[3] = i == 3 ? 0u : key[3];
+            }
+            const int e = wl + 64 * i;
+            sel[j] = e;
+            ordv[j] = m - 1u;
+            if (has_row) row_issue<FMT>(a, my_mat, e, i0 + (wave >> 1), rl[j]);
+            load_down(j, e);
+        }
+    }
+    if (wave == 0 && lane == 0) {
+        float sum = 0.f;
+        for (int j = 0; j < k; j++) {
+            // the logit from its order (inverse of select_key; -0 comes back as +0)
+            const uint32_t o = ordv[j];
+            const float l = __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
+            const float sg = 1.0f / (1.0f + expf(-l));
+            sh.ids[j] = sel[j];
+            sh.wt[j] = sg;
+            sum += sg;
+        }
+        if (a.renorm)
+            for (int j = 0; j < k; j++) sh.wt[j] = sh.wt[j] / sum;
+    }
+    float dts = 1.f;
+    if (FMT == 1 && wave == 0 && lane < ns) {
+        int e = E;
+#pragma unroll
+        for (int j = 0; j < kMaxK; j++)
+            if (j < k && lane == j) e = sel[j];
+        dts = mat_ts(a.w.down, e, E);
+    }
+    if (has_row) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; j++) {
+            if (j < k) {
+                const float v = row_dot<FMT>(a, rl[j], xb, xf);
+                if (lane == 0) ((wave & 1) ? sh.u : sh.g)[j][wave >> 1] = v;
+            }
+        }
+    }
+    if (FMT == 1 && wave == 0 && lane < ns) sh.dts[lane] = dts;
+    __syncthreads();  // also completes this workgroup's HBM -> LDS copies
+    for (int q = tid; q < k * npair; q += 512) {
+        const int j = q / npair, p = q - j * npair;
+        put_word(a.xh + (size_t)j * I + i0 + p, tag, silu(sh.g[j][p]) * sh.u[j][p]);
+    }
+    if (b == 0 && tid < 64) {  // publish the routing tensors (the single token: t = 0)
+        for (int e = tid; e <= E; e += 64) {
+            int below = 0, eq = 0;
+            for (int j = 0; j < k; j++) {
+                below += sh.ids[j] < e;
+                eq += sh.ids[j] == e;
+            }
+            a.offsets[e] = below;
+            if (e < E) a.counts[e] = eq;
+        }
+        if (tid < k) {
+            int pos = 0;
+            for (int j = 0; j < k; j++) pos += sh.ids[j] < sh.ids[tid];
+            a.ids[tid] = sh.ids[tid];
+            a.tw[tid] = sh.wt[tid];
+            a.sa[pos] = tid;
+            a.ap[tid] = pos;
+        }
+    }
+
+    // ---------------- phase 3: down rows from LDS against h, combine
+    {
+        constexpr int NH = (kMaxK + 1) * 1024 / 512;
+        const int nh = ns * I, nq = tid < nh ? (nh - tid + 511) / 512 : 0;
+        uint64_t hw[NH];
+#pragma unroll
+        for (int q = 0; q < NH; q++) hw[q] = q < nq ? get_word(a.xh + tid + 512 * q) : 0ull;
+        await_words<NH>(a.xh + tid, 512, nq, hw, tag, a.ctl);
+#pragma unroll
+        for (int q = 0; q < NH; q++)
+            if (q < nq) sh.hb[tid + 512 * q] = f2bf(__uint_as_float((uint32_t)hw[q]));
+    }
+    __syncthreads();
+    // Wave w takes slot j = w (and j + 8); lane = (row n = lane / 8, part s = lane % 8):
+    // the 8 lanes of row n0 + n take 16-byte units s, s + 8, ... so that every group of
+    // 8 lanes reads 128 contiguous bytes of LDS.
+    {
+        const int n = lane >> 3, s = lane & 7;
+        for (int j = wave; j < ns; j += kWaves) {
+            float acc = 0.f;
+            if (n < rows_h) {
+                const uint8_t *blk = dyn + (size_t)j * cpb * 16;
+                const uint16_t *hj = sh.hb + (size_t)j * I;
+                if (FMT == 0) {
+                    const uint8_t *row = blk + (size_t)n * drow_bytes;
+                    for (int c = s; c < I / 8; c += 8)
+                        acc = dot8_bf16(*reinterpret_cast<const u32x4 *>(row + 16 * c),
+                                        *reinterpret_cast<const u32x4 *>(hj + 8 * c), acc);
+                } else {
+                    const uint8_t *qrow = blk + (size_t)n * (I / 2);
+                    const uint8_t *sf = blk + (size_t)rows_h * (I / 2) + (size_t)n * (I / 16);
+                    for (int c = s; c < I / 16; c += 8) {  // 16-element blocks: 8 code bytes, one scale
+                        const u32x2 q = *reinterpret_cast<const u32x2 *>(qrow + 8 * c);
+                        const uint32_t q0 = q[0], q1 = q[1];
+                        float p = dot8_fp4_bf16(q0, *reinterpret_cast<const u32x4 *>(hj + 16 * c), 0.f);
+                        p = dot8_fp4_bf16(q1, *reinterpret_cast<const u32x4 *>(hj + 16 * c + 8), p);
+                        acc += p * e4m3_to_f32(sf[c]);
+                    }
+                }
+            }
+            // sum over the row's 8 lanes: xor 1, xor 2, then the mirror within 8 lanes
+            acc += __int_as_float(FLINT_DPP(__float_as_int(acc), 0xB1));
+            acc += __int_as_float(FLINT_DPP(__float_as_int(acc), 0x4E));
+            acc += __int_as_float(FLINT_DPP(__float_as_int(acc), 0x141));
+            if (s == 0 && n < rows_h) sh.o[j][n] = FMT == 1 ? acc * sh.dts[j] : acc;
+        }
+    }
+    __syncthreads();
+    for (int n = tid; n < rows_h; n += 512) {
+        float acc = S ? sh.o[k][n] : 0.f;
+        for (int j = 0; j < k; j++) acc += sh.wt[j] * sh.o[j][n];
+        a.y[n0 + n] = (uint16_t)f2bf(acc);
+    }
+}
+
+}  // namespace
+
+// LDS for the down rows of one workgroup's H-slice, all k + S experts.
+static size_t d1_dyn_bytes(const Shape &s, int fmt)
+{
+    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + s.I / 16;
+    return (size_t)(s.k + s.S) * (s.H / kG) * row;
+}
+
+// CU count of the current device, asked once per device.
+static int device_cus()
+{
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+bool decode1_supported(const Shape &s, int fmt)
+{
+    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + s.I / 16;
+    const int rows_h = s.H / kG;
+    return s.H % kG == 0 && s.H <= 2048 &&                   // rows_h <= 8, x in 4 chunks per lane
+           s.I % 32 == 0 && s.I <= 1024 && s.k <= kMaxK &&    // <= 4 gate/up pairs: one row per wave
+           (size_t)rows_h * row % 16 == 0 &&                  // whole 16-byte chunks per block
+           d1_dyn_bytes(s, fmt) + sizeof(D1Shared) <= 160 * 1024 && device_cus() >= kG;
+}
+
+hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, const float *Wr,
+                          const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
+                          int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
+                          hipStream_t st)
+{
+    char *hb = static_cast<char *>(head);
+    D1Args a{s.H, s.I, s.E, s.k, s.S, s.renorm, w, x, Wr, bias, y, logits, ids, tw, counts, offsets,
+             sa, ap, reinterpret_cast<uint32_t *>(hb), reinterpret_cast<uint64_t *>(hb + kXLogOff),
+             reinterpret_cast<uint64_t *>(hb + kXHOff)};
+    const size_t dyn = d1_dyn_bytes(s, w.fmt);
+    // HIP on gfx950 takes up to the CU's 160 KB of LDS per workgroup without an opt-in.
+    if (w.fmt == 0) decode1_kernel<0><<<kG, 512, dyn, st>>>(a);
+    else decode1_kernel<1><<<kG, 512, dyn, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace flint

@@ -116,8 +116,7 @@ class Case:
                 "assign_pos": z(max(T * k, 1)), "y": z(max(T, 1), H, dt=torch.int16)}
 
     def workspace(self, T=None):
-        nb = fm.workspace_bytes(self.desc, self.T if T is None else T, self.fmt)
-        return torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        return fm.workspace(self.desc, self.T if T is None else T, self.fmt)
 
     def run_layer(self):
         out = self.alloc_out()

@@ -109,7 +109,7 @@ def test_route_logits_in_ties_signed_zero_nan():
     dl = torch.from_numpy(lg).cuda()
     ids = torch.zeros((T, k), dtype=torch.int32, device="cuda")
     w = torch.zeros((T, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(fm.workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    ws = fm.workspace(d, T)
     fm.route(d, T, None, None, None, ids, w, ws, logits=dl, logits_in=True)
     torch.cuda.synchronize()
     got = ids.cpu().numpy()
@@ -131,16 +131,16 @@ def test_route_logits_in_ties_signed_zero_nan():
 _FULL = {}
 
 
-def _full_case(T, fmt=fm.WFMT_BF16, bias_c=None):
+def _full_case(T, fmt=fm.WFMT_BF16, bias_c=None, layer=0, routed_only=False):
     H, I, E, k = 2048, 768, 256, 6
-    if fmt == fm.WFMT_BF16:
-        return Case(T, H, I, E, k, bias_c=bias_c)
-    # NVFP4: quantise only the experts the reference routing touches; the others hold
-    # zero codes, identically on both sides.
-    x = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), 1.0)
-    Wr = dg.normal_f32((E, H), 0, dg.stream_id(0, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+    if fmt == fm.WFMT_BF16 and not routed_only:
+        return Case(T, H, I, E, k, bias_c=bias_c, layer=layer)
+    # Only the experts the reference routing touches get weights; the others hold zeros,
+    # identically on both sides (a wrongly chosen expert would still show up as a mismatch).
+    x = dg.normal_bf16((T, H), 0, dg.stream_id(layer, dg.KIND_X, 0), 1.0)
+    Wr = dg.normal_f32((E, H), 0, dg.stream_id(layer, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
     ids = oracle.select(oracle.router(x, Wr), k)
-    return Case(T, H, I, E, k, fmt=fmt, experts=sorted(set(ids.reshape(-1).tolist())))
+    return Case(T, H, I, E, k, fmt=fmt, layer=layer, experts=sorted(set(ids.reshape(-1).tolist())))
 
 
 @pytest.mark.parametrize("T", [1, 8, 32])
@@ -158,3 +158,28 @@ def test_full_prefill_8192(zipf):
     c = _full_case(8192, bias_c=dg.ZIPF_C if zipf else None)
     toks = np.unique(np.concatenate([np.arange(0, 8192, 523), [8191]])).astype(np.int64)
     _parity(c, tokens=toks)
+
+
+@pytest.mark.parametrize("fmt", [fm.WFMT_BF16, fm.WFMT_NVFP4])
+def test_single_token_launch_reuses_workspace(fmt):
+    """T = 1 runs as one persistent launch whose workgroups exchange logits and h through
+    launch-tagged words at the start of the workspace: consecutive calls on one workspace
+    (each reading words the previous call tagged) all match the reference, the launch
+    counter advances by one per call and no wait ever timed out."""
+    d = fm.desc(2048, 768)
+    ws = fm.workspace(d, 1, fmt)
+    for n_call, layer in enumerate((0, 1, 2, 3, 0)):
+        c = _full_case(1, fmt=fmt, layer=layer, routed_only=True).upload()
+        out = c.alloc_out()
+        routing = {kk: out[kk] for kk in ("logits", "topk_ids", "topk_w", "counts", "offsets",
+                                          "sorted_assign", "assign_pos")}
+        fm.layer(c.desc, c.weights, 1, c.d_x, c.d_Wr, None, out["y"], ws, routing)
+        torch.cuda.synchronize()
+        from moe_cases import to_host
+        g = to_host(out, c)
+        w64 = check_routing(c, g)
+        rm, rl = check_forward(c, g, w64)
+        head = ws[:8].view(torch.int32).cpu().numpy()
+        assert head[1] == 0, "a wait timed out"
+        assert head[0] == n_call + 1, head
+        _say("layer %d fmt %d: max rel %.2e rel L1 %.2e" % (layer, fmt, rm, rl))
