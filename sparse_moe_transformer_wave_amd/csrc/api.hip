@@ -120,7 +120,7 @@ WsLayout ws_layout(const Shape &s, int64_t T)
     L.offsets = take((size_t)(s.E + 1) * 4);
     L.sa = take(TK * 4);
     L.ap = take(TK * 4);
-    L.plan = take((size_t)(4 + 3 * (s.E + 1) + L.max_items + s.H / 16) * 4);
+    L.plan = take((size_t)(4 + 3 * (s.E + 1) + L.max_items) * 4);
     L.hist = take(((TK + 1023) / 1024) * (size_t)s.E * 4);
     L.h = take(slots * s.I * 4);
     L.o = take(slots * s.H * 4);
@@ -137,7 +137,6 @@ Plan plan_view(void *ws, const WsLayout &L, const Shape &s)
     p.tbase = p.touched + (s.E + 1);
     p.tcount = p.tbase + (s.E + 1);
     p.items = p.tcount + (s.E + 1);
-    p.counters = p.items + L.max_items;
     return p;
 }
 
@@ -239,13 +238,12 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
 
 static int forward_impl(const Shape &s, const WSet &wset, int64_t T, const uint16_t *x,
                         const float *topk_w, const int32_t *sa, const int32_t *ap, uint16_t *y,
-                        void *ws, const WsLayout &L, const Plan &plan, hipStream_t st,
-                        const RouteOut *route = nullptr)
+                        void *ws, const WsLayout &L, const Plan &plan, hipStream_t st)
 {
     char *b = (char *)ws;
     if (T <= kGemvMaxT) {
         return hip_status(launch_gemv_forward(s, wset, T, x, topk_w, sa, ap, plan,
-                                              (uint16_t *)(b + L.h), y, route, st));
+                                              (uint16_t *)(b + L.h), y, st));
     }
     return hip_status(launch_gemm_forward(s, wset, T, x, topk_w, sa, ap, plan,
                                           (uint16_t *)(b + L.h), (uint16_t *)(b + L.o), y, st));
@@ -318,16 +316,13 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
         return hip_status(launch_decode1(s, wset_of(weights), x, w_router, logit_bias, y, lg, ids, tw,
                                          cnt, off, sa, ap, b + L.sync, st));
     }
-    rc = hip_status(launch_router(s, T, x, w_router, logit_bias, lg, st));
-    if (rc) return rc;
-    if (T <= kFusedSelectMaxT) {
-        const RouteOut ro{lg, ids, tw, cnt, off, sa, ap};
-        return forward_impl(s, wset_of(weights), T, x, tw, sa, ap, y, ws, L, plan, st, &ro);
-    }
     if (T <= kGemvMaxT) {
-        rc = hip_status(launch_select_permute(s, T, lg, ids, tw, cnt, off, sa, ap, plan, st));
+        rc = hip_status(launch_router_select(s, T, x, w_router, logit_bias, lg, ids, tw, cnt, off,
+                                             sa, ap, plan, (int *)(b + L.sync) + 2, st));
         if (rc) return rc;
     } else {
+        rc = hip_status(launch_router(s, T, x, w_router, logit_bias, lg, st));
+        if (rc) return rc;
         rc = hip_status(launch_topk(s, T, lg, ids, tw, st));
         if (rc) return rc;
         rc = hip_status(launch_permute(s, T, ids, cnt, off, sa, ap, &plan,

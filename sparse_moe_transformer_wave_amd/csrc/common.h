@@ -48,7 +48,6 @@ struct Plan {
     int *meta;
     int *touched, *tbase, *tcount;
     int *items;
-    int *counters;
 };
 
 // Workspace carve-up (byte offsets from the workspace base), computed on the host.
@@ -72,10 +71,13 @@ hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t
                           int32_t *hist, hipStream_t st);
 hipError_t launch_plan(const Shape &s, int64_t T, const int32_t *offsets, const Plan &plan,
                        hipStream_t st);
-// T <= kGemvMaxT: top-k, grouping and plan in one workgroup.
-hipError_t launch_select_permute(const Shape &s, int64_t T, const float *logits, int32_t *ids,
-                                 float *w, int32_t *counts, int32_t *offsets, int32_t *sa,
-                                 int32_t *ap, const Plan &plan, hipStream_t st);
+// 2 <= T <= kGemvMaxT: router, then (in the last workgroup to finish) top-k, grouping and
+// plan, in one launch.  `arrivals` = a zero-initialised word of the workspace head; every
+// launch leaves it zero.
+hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, const float *Wr,
+                                const float *bias, float *logits, int32_t *ids, float *w,
+                                int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap,
+                                const Plan &plan, int *arrivals, hipStream_t st);
 // Single-token layer in one persistent launch (decode1.hip).  `head` = the workspace's
 // first kSyncBytes (launch counter and exchange words; zero before first use).
 // decode1_supported also checks that the current device has a CU for every workgroup.
@@ -86,20 +88,10 @@ hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, cons
                           int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
                           hipStream_t st);
 
-// Routing outputs a fused small-batch launch writes (workgroup 0) for later kernels.
-struct RouteOut {
-    const float *logits;
-    int32_t *ids;
-    float *w;
-    int32_t *counts, *offsets, *sa, *ap;
-};
-// Streaming path.  With `route` non-null (T <= kFusedSelectMaxT), the gate/up kernel
-// selects and groups from route->logits itself; otherwise the plan must already exist.
-constexpr int kFusedSelectMaxT = 8;
+// Streaming path (T <= kGemvMaxT) from an existing plan.
 hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
-                               const Plan &plan, uint16_t *h, uint16_t *y, const RouteOut *route,
-                               hipStream_t st);
+                               const Plan &plan, uint16_t *h, uint16_t *y, hipStream_t st);
 hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
                                const Plan &plan, uint16_t *h, uint16_t *o, uint16_t *y,
@@ -175,6 +167,70 @@ __device__ __forceinline__ float wave_sum(float v)
     return (a + b) + (c + d);
 }
 
+// Router products of expert row e with the tokens t = t0 + ts q (q < TW, t < T), by one
+// wave: a lane owns 8 consecutive h per 2048-wide slice (two float4 of the fp32 row and
+// 16 bytes of each token's bf16 x), every load of a slice in flight together; out[q] =
+// the fp32 sum over H (DPP-reduced, valid in every lane).
+template <int TW>
+__device__ __forceinline__ void router_dot_wave(int T, int H, int e, int t0, int ts,
+                                                const uint16_t *__restrict__ x,
+                                                const float *__restrict__ Wr, float *out)
+{
+    const int lane = threadIdx.x & 63;
+    float acc[TW];
+#pragma unroll
+    for (int q = 0; q < TW; q++) acc[q] = 0.f;
+    const float4 *w4 = reinterpret_cast<const float4 *>(Wr + (size_t)e * H);
+    const int nc = H / 8;  // 8-element chunks per row
+    for (int c0 = 0; c0 < nc; c0 += 256) {
+        float4 w[8];
+        u32x4 xv[TW][4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int c = c0 + lane + 64 * i;
+            if (c < nc) {
+                w[2 * i] = w4[2 * c];
+                w[2 * i + 1] = w4[2 * c + 1];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < TW; q++) {
+            const int t = t0 + ts * q;
+            if (t < T)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int c = c0 + lane + 64 * i;
+                    if (c < nc) xv[q][i] = *reinterpret_cast<const u32x4 *>(x + (size_t)t * H + 8 * c);
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < TW; q++) {
+            const int t = t0 + ts * q;
+            if (t < T)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int c = c0 + lane + 64 * i;
+                    if (c < nc) {
+                        const float4 a = w[2 * i], b = w[2 * i + 1];
+                        const uint32_t x0 = xv[q][i][0], x1 = xv[q][i][1], x2 = xv[q][i][2], x3 = xv[q][i][3];
+                        float sum = acc[q];
+                        sum += bf2f(x0 & 0xffffu) * a.x;
+                        sum += bf2f(x0 >> 16) * a.y;
+                        sum += bf2f(x1 & 0xffffu) * a.z;
+                        sum += bf2f(x1 >> 16) * a.w;
+                        sum += bf2f(x2 & 0xffffu) * b.x;
+                        sum += bf2f(x2 >> 16) * b.y;
+                        sum += bf2f(x3 & 0xffffu) * b.z;
+                        sum += bf2f(x3 >> 16) * b.w;
+                        acc[q] = sum;
+                    }
+                }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < TW; q++) out[q] = t0 + ts * q < T ? wave_sum(acc[q]) : 0.f;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     v = max(v, (uint32_t)FLINT_DPP((int)v, 0xB1));
@@ -211,31 +267,38 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return ((uint64_t)mh << 32) | ml;
 }
 
-// Called by a whole wave.  Each lane holds experts lane, lane+64, lane+128, lane+192;
-// k rounds of a wave-wide arg-max, the winning lane retires its entry.  Lane 0 writes
-// ids[0..k) and the sigmoid weights (renormalised to sum 1 if renorm).
+// Called by a whole wave.  Each lane holds experts lane, lane+64, lane+128, lane+192 as
+// 32-bit keys: the order of the logit (select_key's high word) plus one, 0 = no expert or
+// already taken, so a NaN logit (order 0) still ranks above those.  k rounds of a DPP max;
+// among equal keys the lowest expert wins: the first i with a match, the lowest lane in
+// it (ballots).  Lane 0 writes ids[0..k) and the sigmoid weights (renormalised to sum 1
+// if renorm).
 __device__ __forceinline__ void topk_token(const float *__restrict__ lg, int E, int k, int renorm,
                                            int32_t *__restrict__ ids, float *__restrict__ wout)
 {
     const int lane = threadIdx.x & 63;
-    uint64_t key[4];
+    uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        int e = lane + 64 * i;
-        key[i] = (e < E) ? select_key(lg[e], e) : 0ull;
+        const int e = lane + 64 * i;
+        key[i] = e < E ? (uint32_t)(select_key(lg[e], e) >> 32) + 1u : 0u;
     }
     int sel_id[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         if (j >= k) break;
-        uint64_t m = key[0];
-#pragma unroll
-        for (int i = 1; i < 4; i++) m = key[i] > m ? key[i] : m;
-        uint64_t best = wave_max_u64(m);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            if (key[i] == best) key[i] = 0ull;
-        sel_id[j] = (int)(0xffffu - (uint32_t)(best & 0xffffu));
+        const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+        const uint64_t b0 = __ballot(key[0] == m), b1 = __ballot(key[1] == m);
+        const uint64_t b2 = __ballot(key[2] == m), b3 = __ballot(key[3] == m);
+        const int i = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
+        const int wl = __builtin_ctzll(b0 ? b0 : b1 ? b1 : b2 ? b2 : b3);
+        if (lane == wl) {
+            key[0] = i == 0 ? 0u : key[0];
+            key[1] = i == 1 ? 0u : key[1];
+            key[2] = i == 2 ? 0u : key[2];
+            key[3] = i == 3 ? 0u : key[3];
+        }
+        sel_id[j] = wl + 64 * i;
     }
     if (lane == 0) {
         float sg[8];

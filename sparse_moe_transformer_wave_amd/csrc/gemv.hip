@@ -10,11 +10,13 @@
 // Pass 1 (gate/up): one workgroup per (touched expert, 8 rows of I).  Its B operand holds
 //   8 gate rows in MFMA columns 0-7 and the same 8 up rows in columns 8-15, so one MFMA
 //   produces g and u side by side; the 4 waves split K and meet in LDS; h = silu(g) * u is
-//   rounded to bf16.  For T <= 8 every workgroup first selects and groups the tokens'
-//   experts itself from the router logits (a few hundred instructions), which saves the
-//   launch of a separate routing kernel; workgroup 0 publishes the routing tensors.
-// Pass 2 (down + combine): one workgroup per 16 rows of H, covering every touched expert
-//   (one wave per expert at a time, all of its weight and h loads in flight together).
+//   rounded to bf16.  The expert's token rows form the MFMA A operand; lanes whose row is
+//   past the expert's token count load nothing (most routed experts of a decode step hold
+//   one or two tokens).
+// Pass 2 (down + combine): one workgroup per 8 rows of H (H / 8 = 256 workgroups at
+//   H = 2048, one per CU), covering every touched expert (one wave per expert at a time,
+//   all of its weight and h loads in flight together).  The 8 rows fill MFMA columns 0-7;
+//   columns 8-15 stay zero and load nothing.
 //   Per-slot outputs stay in LDS in fp32 and the workgroup combines them (shared first,
 //   then the k routed slots in order) into bf16 y, so no other workgroup is waited for.
 #include "common.h"
@@ -39,110 +41,32 @@ __device__ __forceinline__ float expert_ts(const WMat &m, int e, int E)
 }
 
 // ------------------------------------------------------------------ pass 1: gate / up
-// Top-k of the T <= 8 tokens (wave t takes tokens t, t + 4) and their grouping, in LDS.
-// The publishing workgroup also writes the routing tensors and the plan for the down pass.
-struct FusedRoute {
-    int32_t ids[64];
-    float w[64];
-    int slot[64];
-    int touched[72], tbase[72], tcount[72];
-    int nT;
-};
-
-__device__ void fused_select(int T, int E, int k, int S, int renorm, const RouteOut &ro,
-                             const Plan &p, FusedRoute &fr, bool publish)
-{
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int t = wave; t < T; t += 4)
-        topk_token(ro.logits + (size_t)t * E, E, k, renorm, fr.ids + t * k, fr.w + t * k);
-    __syncthreads();
-    if (wave == 0) {
-        const int nT = wave_group_small(T * k, T, k, E, S, fr.ids, fr.touched, fr.tbase, fr.tcount, fr.slot);
-        if (lane == 0) fr.nT = nT;
-    }
-    __syncthreads();
-    if (!publish) return;
-    const int n = T * k;
-    for (int a = tid; a < n; a += 256) {
-        ro.ids[a] = fr.ids[a];
-        ro.w[a] = fr.w[a];
-        ro.sa[fr.slot[a]] = a;
-        ro.ap[a] = fr.slot[a];
-    }
-    for (int e = tid; e <= E; e += 256) {
-        int below = 0, eq = 0;
-        for (int a = 0; a < n; a++) {
-            below += fr.ids[a] < e;
-            eq += fr.ids[a] == e;
-        }
-        ro.offsets[e] = below;
-        if (e < E) ro.counts[e] = eq;
-    }
-    for (int u = tid; u < fr.nT; u += 256) {
-        p.touched[u] = fr.touched[u];
-        p.tbase[u] = fr.tbase[u];
-        p.tcount[u] = fr.tcount[u];
-    }
-    if (tid == 0) p.meta[0] = fr.nT;
-}
-
-template <int FMT, int NMT, bool FUSED>
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, int E, int k, int S,
-                                                          int renorm, WSet w,
+template <int FMT, int NMT>
+__global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, int E, int k, WSet w,
                                                           const uint16_t *__restrict__ x,
                                                           const int32_t *__restrict__ sa_in,
-                                                          Plan p, RouteOut ro,
-                                                          uint16_t *__restrict__ h)
+                                                          Plan p, uint16_t *__restrict__ h)
 {
     __shared__ float red[4][NMT][64][4];
     const int nrb = I / 8;
     const int u = blockIdx.x / nrb, rb = blockIdx.x - u * nrb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    int e, base, cnt;
-    const uint16_t *xr[NMT];
-    if (FUSED) {
-        // Unit 0 is the shared expert (all T tokens): its workgroups need no routing and
-        // start streaming at once; routed units u >= S select first.  The first routed
-        // unit's first workgroup publishes the routing tensors.
-        if (S && u == 0) {
-            e = E;
-            base = T * k;
-            cnt = T;
+    // The unit's plan entry loads together with the unit count (one round trip), then the
+    // token indices of the A rows together with the first weights (one more).
+    const int nT = p.meta[0];
+    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    if (u >= nT) return;
+    int tix[NMT];
 #pragma unroll
-            for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)min(mt * 16 + r, cnt - 1) * H;
-        } else {
-            __shared__ FusedRoute fr;
-            fused_select(T, E, k, S, renorm, ro, p, fr, blockIdx.x == (unsigned)(S * nrb));
-            const int ur = u - S;
-            if (ur >= fr.nT - S) return;
-            e = fr.touched[ur];
-            base = fr.tbase[ur];
-            cnt = fr.tcount[ur];
-            // token of slot base + i: the assignment whose slot it is
-#pragma unroll
-            for (int mt = 0; mt < NMT; mt++) {
-                const int idx = min(mt * 16 + r, cnt - 1);
-                int tok = idx;
-                for (int a = 0; a < T * k; a++)
-                    if (fr.slot[a] == base + idx) tok = a / k;
-                xr[mt] = x + (size_t)tok * H;
-            }
-        }
-    } else {
-        if (u >= p.meta[0]) return;
-        e = p.touched[u];
-        base = p.tbase[u];
-        cnt = p.tcount[u];
-#pragma unroll
-        for (int mt = 0; mt < NMT; mt++) {
-            const int idx = min(mt * 16 + r, cnt - 1);
-            const int tok = (e == E) ? idx : sa_in[base + idx] / k;
-            xr[mt] = x + (size_t)tok * H;
-        }
+    for (int mt = 0; mt < NMT; mt++) {
+        const int idx = min(mt * 16 + r, cnt - 1);
+        tix[mt] = (e == E) ? idx * k : sa_in[base + idx];  // assignment index; token = tix / k
     }
-    const bool sh = (e == E);
-    (void)sh;
+    const uint16_t *xr[NMT];
     const int nmt = (cnt + 15) >> 4;
+    bool has_tok[NMT];  // this lane's A row is one of the expert's tokens
+#pragma unroll
+    for (int mt = 0; mt < NMT; mt++) has_tok[mt] = mt * 16 + r < cnt;
     const int i0 = rb * 8;
     const int row = i0 + (r & 7);           // gate row (lanes r < 8) or up row (r >= 8)
     const WMat &wm = (r < 8) ? w.gate : w.up;
@@ -156,15 +80,22 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
         const int kq = wave * cpw * 32 + g * 8;
         constexpr int NB = 16;
         int c0 = 0;
-        for (; c0 + NB <= cpw; c0 += NB) {   // full batches: every load issued, no branches
-            u32x4 b[NB], a[NMT][NB];
+        u32x4 b[NB];
+        if (NB <= cpw)  // the first batch of weights goes out before the token rows resolve
 #pragma unroll
-            for (int i = 0; i < NB; i++) b[i] = ld16(W + kq + (c0 + i) * 32);
+            for (int i = 0; i < NB; i++) b[i] = ld16(W + kq + i * 32);
+#pragma unroll
+        for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)(tix[mt] / k) * H;
+        for (; c0 + NB <= cpw; c0 += NB) {   // full batches: every load issued, no branches
+            u32x4 a[NMT][NB];
+            if (c0 > 0)
+#pragma unroll
+                for (int i = 0; i < NB; i++) b[i] = ld16(W + kq + (c0 + i) * 32);
 #pragma unroll
             for (int mt = 0; mt < NMT; mt++)
                 if (NMT == 1 || mt < nmt)
 #pragma unroll
-                    for (int i = 0; i < NB; i++) a[mt][i] = ld16(xr[mt] + kq + (c0 + i) * 32);
+                    for (int i = 0; i < NB; i++) a[mt][i] = has_tok[mt] ? ld16(xr[mt] + kq + (c0 + i) * 32) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < NB; i++)
 #pragma unroll
@@ -175,13 +106,16 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
             const u32x4 b = ld16(W + kq + c0 * 32);
 #pragma unroll
             for (int mt = 0; mt < NMT; mt++)
-                if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(ld16(xr[mt] + kq + c0 * 32)), as_bf16x8(b), acc[mt]);
+                if (NMT == 1 || mt < nmt)
+                    acc[mt] = mfma16x16x32(as_bf16x8(has_tok[mt] ? ld16(xr[mt] + kq + c0 * 32) : u32x4{0u, 0u, 0u, 0u}), as_bf16x8(b), acc[mt]);
         }
     } else {
         // NVFP4: per 128-wide super-chunk a lane takes 32 consecutive k of its row (16
         // bytes of codes, 2 block scales); MFMA j consumes the lane's k + 8j .. k + 8j + 7.
         const uint8_t *Q = expert_base(wm, e, E, (size_t)I * H / 2) + (size_t)row * (H / 2);
         const uint8_t *SF = expert_sf(wm, e, E, (size_t)I * H / 16) + (size_t)row * (H / 16);
+#pragma unroll
+        for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)(tix[mt] / k) * H;
         const int nsc = H / 128;
         constexpr int NB = 4;
         for (int s0 = wave; s0 < nsc; s0 += 4 * NB) {
@@ -204,7 +138,8 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
                         const int sc = s0 + 4 * i;
                         if (sc < nsc)
 #pragma unroll
-                            for (int j = 0; j < 4; j++) a[mt][i][j] = ld16(xr[mt] + sc * 128 + g * 32 + 8 * j);
+                            for (int j = 0; j < 4; j++)
+                                a[mt][i][j] = has_tok[mt] ? ld16(xr[mt] + sc * 128 + g * 32 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
                     }
 #pragma unroll
             for (int i = 0; i < NB; i++) {
@@ -254,13 +189,22 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
                                                         const int32_t *__restrict__ ap, Plan p,
                                                         uint16_t *__restrict__ y)
 {
-    __shared__ float o_lds[kGemvMaxT * 8 + kGemvMaxT][16];
-    const int n0 = blockIdx.x * 16;
-    const int nT = p.meta[0];
+    __shared__ float o_lds[kGemvMaxT * 8 + kGemvMaxT][8];
+    __shared__ int s_e[257], s_base[257], s_cnt[257], s_nT;
+    const int n0 = blockIdx.x * 8;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    const int row = n0 + r;
+    // The plan, once, into LDS: the expert loop below then never waits on global memory
+    // before it can issue an expert's weight loads.
+    for (int u = tid; u < E + S; u += 512) {
+        s_e[u] = p.touched[u];
+        s_base[u] = p.tbase[u];
+        s_cnt[u] = p.tcount[u];
+    }
+    if (tid == 0) s_nT = p.meta[0];
+    const bool on_row = r < 8;  // MFMA column r holds row n0 + r
+    const int row = n0 + (r & 7);
     // The combine inputs of this thread's (token, column), fetched before the weights.
-    const int ct = tid >> 4;
+    const int ct = tid >> 3;
     float cw[8];
     int cslot[8];
 #pragma unroll
@@ -269,12 +213,18 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
         cw[jj] = on ? topk_w[ct * k + jj] : 0.f;
         cslot[jj] = on ? ap[ct * k + jj] : 0;
     }
+    __syncthreads();
+    const int nT = s_nT;
     for (int u = wave; u < nT; u += 8) {
-        const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+        const int e = s_e[u], base = s_base[u], cnt = s_cnt[u];
         const int nmt = (cnt + 15) >> 4;
         const uint16_t *hr[NMT];
+        bool has_tok[NMT];  // this lane's A row is one of the expert's tokens
 #pragma unroll
-        for (int mt = 0; mt < NMT; mt++) hr[mt] = h + (size_t)(base + min(mt * 16 + r, cnt - 1)) * I;
+        for (int mt = 0; mt < NMT; mt++) {
+            hr[mt] = h + (size_t)(base + min(mt * 16 + r, cnt - 1)) * I;
+            has_tok[mt] = mt * 16 + r < cnt;
+        }
         f32x4 acc[NMT];
 #pragma unroll
         for (int mt = 0; mt < NMT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -288,12 +238,12 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
             for (; c0 + NB <= nch; c0 += NB) {   // full batches: every load issued, no branches
                 u32x4 b[NB], a[NMT][NB];
 #pragma unroll
-                for (int i = 0; i < NB; i++) b[i] = ld16(Wd + (c0 + i) * 32 + g * 8);
+                for (int i = 0; i < NB; i++) b[i] = on_row ? ld16(Wd + (c0 + i) * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int mt = 0; mt < NMT; mt++)
                     if (NMT == 1 || mt < nmt)
 #pragma unroll
-                        for (int i = 0; i < NB; i++) a[mt][i] = ld16(hr[mt] + (c0 + i) * 32 + g * 8);
+                        for (int i = 0; i < NB; i++) a[mt][i] = has_tok[mt] ? ld16(hr[mt] + (c0 + i) * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int i = 0; i < NB; i++)
 #pragma unroll
@@ -301,10 +251,11 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
                         if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i]), as_bf16x8(b[i]), acc[mt]);
             }
             for (; c0 < nch; c0++) {               // tail
-                const u32x4 b = ld16(Wd + c0 * 32 + g * 8);
+                const u32x4 b = on_row ? ld16(Wd + c0 * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int mt = 0; mt < NMT; mt++)
-                    if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(ld16(hr[mt] + c0 * 32 + g * 8)), as_bf16x8(b), acc[mt]);
+                    if (NMT == 1 || mt < nmt)
+                        acc[mt] = mfma16x16x32(as_bf16x8(has_tok[mt] ? ld16(hr[mt] + c0 * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u}), as_bf16x8(b), acc[mt]);
             }
         } else {
             const uint8_t *Qd = expert_base(w.down, e, E, (size_t)H * I / 2) + (size_t)row * (I / 2);
@@ -317,7 +268,9 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
                 uint32_t sb[NB];
 #pragma unroll
                 for (int i = 0; i < NB; i++) {
-                    if (s0 + i < nsc) {
+                    q[i] = u32x4{0u, 0u, 0u, 0u};
+                    sb[i] = 0u;
+                    if (s0 + i < nsc && on_row) {
                         const int kb = (s0 + i) * 128 + g * 32;
                         q[i] = ld16(Qd + kb / 2);
                         sb[i] = *reinterpret_cast<const uint16_t *>(Sd + kb / 16);
@@ -330,7 +283,8 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
                         for (int i = 0; i < NB; i++)
                             if (s0 + i < nsc)
 #pragma unroll
-                                for (int j = 0; j < 4; j++) a[mt][i][j] = ld16(hr[mt] + (s0 + i) * 128 + g * 32 + 8 * j);
+                                for (int j = 0; j < 4; j++)
+                                    a[mt][i][j] = has_tok[mt] ? ld16(hr[mt] + (s0 + i) * 128 + g * 32 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int i = 0; i < NB; i++) {
                     if (s0 + i < nsc) {
@@ -351,12 +305,12 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int ti = mt * 16 + 4 * g + i;
-                if ((NMT == 1 || mt < nmt) && ti < cnt) o_lds[base + ti][r] = acc[mt][i] * ts;
+                if ((NMT == 1 || mt < nmt) && ti < cnt && on_row) o_lds[base + ti][r] = acc[mt][i] * ts;
             }
     }
     __syncthreads();
-    if (ct < T) {  // T * 16 <= 512 threads: one (token, column) each
-        const int n = tid & 15;
+    if (ct < T) {  // T * 8 <= 512 threads: one (token, column) each
+        const int n = tid & 7;
         float acc_y = S ? o_lds[T * k + ct][n] : 0.f;
 #pragma unroll
         for (int jj = 0; jj < 8; jj++)
@@ -365,37 +319,30 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(int T, int H, int I, int
     }
 }
 
-template <int NMT, bool FUSED>
+template <int NMT>
 static void launch_pair(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                         const float *topk_w, const int32_t *sa, const int32_t *ap,
-                        const Plan &plan, uint16_t *h, uint16_t *y, const RouteOut &ro,
-                        hipStream_t st)
+                        const Plan &plan, uint16_t *h, uint16_t *y, hipStream_t st)
 {
     const int maxU = (int)std::min<int64_t>(T * s.k, s.E) + s.S;
-    const unsigned g1 = (unsigned)(maxU * (s.I / 8)), g2 = (unsigned)(s.H / 16);
+    const unsigned g1 = (unsigned)(maxU * (s.I / 8)), g2 = (unsigned)(s.H / 8);
     if (w.fmt == 0) {
-        gemv_gateup_kernel<0, NMT, FUSED><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, s.renorm,
-                                                              w, x, sa, plan, ro, h);
+        gemv_gateup_kernel<0, NMT><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         gemv_down_kernel<0, NMT><<<g2, 512, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, w, h, topk_w, ap, plan, y);
     } else {
-        gemv_gateup_kernel<1, NMT, FUSED><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, s.renorm,
-                                                              w, x, sa, plan, ro, h);
+        gemv_gateup_kernel<1, NMT><<<g1, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         gemv_down_kernel<1, NMT><<<g2, 512, 0, st>>>((int)T, s.H, s.I, s.E, s.k, s.S, w, h, topk_w, ap, plan, y);
     }
 }
 
 hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
-                               const Plan &plan, uint16_t *h, uint16_t *y, const RouteOut *route,
-                               hipStream_t st)
+                               const Plan &plan, uint16_t *h, uint16_t *y, hipStream_t st)
 {
-    const RouteOut ro = route ? *route : RouteOut{};
-    if (route && T <= kFusedSelectMaxT)
-        launch_pair<1, true>(s, w, T, x, route->w, route->sa, route->ap, plan, h, y, ro, st);
-    else if (T <= 16)
-        launch_pair<1, false>(s, w, T, x, topk_w, sa, ap, plan, h, y, ro, st);
+    if (T <= 16)
+        launch_pair<1>(s, w, T, x, topk_w, sa, ap, plan, h, y, st);
     else
-        launch_pair<2, false>(s, w, T, x, topk_w, sa, ap, plan, h, y, ro, st);
+        launch_pair<2>(s, w, T, x, topk_w, sa, ap, plan, h, y, st);
     return hipGetLastError();
 }
 

@@ -70,7 +70,6 @@ __device__ void build_plan(int T, int E, int k, int S, int H, const int *cnt, co
         p.meta[0] = nT;
         p.meta[1] = ps.base[nT];
     }
-    for (int i = tid; i < H / 16; i += bd) p.counters[i] = 0;
 }
 
 // Grouping of n assignments by expert, by one workgroup of 1024 threads.  Assignments are
@@ -154,35 +153,115 @@ __global__ __launch_bounds__(1024) void permute_kernel(int T, int E, int k, int 
     if (with_plan) build_plan(T, E, k, S, H, g.cnt, g.off, plan, ps);
 }
 
-// Small batches (T <= 32): top-k of every token (one wave per token), the grouping and
-// the plan in a single workgroup, so routing costs one launch after the router.
-__global__ __launch_bounds__(1024) void select_permute_kernel(
-    int T, int E, int k, int S, int H, int renorm, const float *__restrict__ logits,
-    int32_t *__restrict__ ids, float *__restrict__ wout, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sa, int32_t *__restrict__ ap, Plan plan)
+// Grouping and plan for n = T * k <= 256 assignments by one 1024-thread workgroup, all in
+// LDS: per-expert counts (LDS atomics), exclusive offsets, and the stable position of
+// assignment a = the offset of its expert plus the number of earlier assignments of the
+// same expert.  Plan: touched experts ascending, the shared expert (all T tokens) last,
+// one work item each (no expert holds more than kGemvMaxT * 8 rows).
+struct SmallGroup {
+    int cnt[257], off[258], flag[257], idx[258];
+};
+
+__device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_ids, SmallGroup &g,
+                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                 int32_t *__restrict__ sa, int32_t *__restrict__ ap, const Plan &p)
 {
-    __shared__ GroupScratch g;
-    __shared__ PlanScratch ps;
+    const int tid = threadIdx.x, n = T * k;
+    if (tid < E) g.cnt[tid] = 0;
+    __syncthreads();
+    const int e = tid < n ? s_ids[tid] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (valid) atomicAdd(&g.cnt[e], 1);
+    __syncthreads();
+    if (tid < 64) wave0_exclusive_scan(g.cnt, g.off, E);
+    __syncthreads();
+    if (tid < E) {
+        counts[tid] = g.cnt[tid];
+        offsets[tid] = g.off[tid];
+    }
+    if (tid == 0) offsets[E] = g.off[E];
+    if (valid) {
+        int before = 0;
+        for (int a = 0; a < tid; a++) before += s_ids[a] == e;
+        const int pos = g.off[e] + before;
+        sa[pos] = tid;
+        ap[tid] = pos;
+    }
+    const int nf = E + S;
+    if (tid < nf) g.flag[tid] = tid < E ? (g.cnt[tid] > 0) : 1;
+    __syncthreads();
+    if (tid < 64) wave0_exclusive_scan(g.flag, g.idx, nf);
+    __syncthreads();
+    if (tid < nf && g.flag[tid]) {
+        const int u = g.idx[tid];
+        p.touched[u] = tid;
+        p.tbase[u] = tid < E ? g.off[tid] : T * k;
+        p.tcount[u] = tid < E ? g.cnt[tid] : T;
+        p.items[u] = u << 16;
+    }
+    if (tid == 0) {
+        p.meta[0] = g.idx[nf];
+        p.meta[1] = g.idx[nf];
+    }
+}
+
+// Small batches (2 <= T <= 32): router and routing in one launch.  Workgroup e (16 waves,
+// wave w takes tokens w and w + 16) computes the logits of expert e and writes them with
+// agent-scope write-through stores; once they have completed it counts itself in at an
+// agent-scope arrival counter.  The workgroup that arrives last has every logit: it reads
+// them back with agent-scope loads into LDS, selects the top-k of every token (one wave
+// per token), groups the assignments by expert and writes the plan, so the expert
+// kernels that follow need no routing step of their own.  It also re-arms the counter.
+__global__ __launch_bounds__(1024) void router_select_kernel(
+    int T, int H, int E, int k, int S, int renorm, const uint16_t *__restrict__ x,
+    const float *__restrict__ Wr, const float *__restrict__ bias, float *__restrict__ logits,
+    int32_t *__restrict__ ids, float *__restrict__ wout, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sa, int32_t *__restrict__ ap, Plan plan,
+    int *arrivals)
+{
+    __shared__ SmallGroup g;
+    __shared__ float s_lg[kGemvMaxT * 256];
     __shared__ int32_t s_ids[kGemvMaxT * 8];
     __shared__ float s_w[kGemvMaxT * 8];
-    const int wv = threadIdx.x >> 6;
-    for (int t = wv; t < T; t += 16)
-        topk_token(logits + (size_t)t * E, E, k, renorm, s_ids + t * k, s_w + t * k);
+    __shared__ int s_last;
+    const int e = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    float sums[2];
+    router_dot_wave<2>(T, H, e, wv, 16, x, Wr, sums);
+    const float bv = bias ? bias[e] : 0.f;
+    if (lane == 0)
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int t = wv + 16 * q;
+            if (t < T)
+                __hip_atomic_store(logits + (size_t)t * E + e, sums[q] + bv, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's logit stores have completed
     __syncthreads();
-    for (int a = threadIdx.x; a < T * k; a += 1024) {
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = tid; i < T * E; i += 1024)
+        s_lg[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(arrivals, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    for (int t = wv; t < T; t += 16) topk_token(s_lg + t * E, E, k, renorm, s_ids + t * k, s_w + t * k);
+    __syncthreads();
+    for (int a = tid; a < T * k; a += 1024) {
         ids[a] = s_ids[a];
         wout[a] = s_w[a];
     }
-    group_by_expert(T * k, E, s_ids, g, counts, offsets, sa, ap);
-    build_plan(T, E, k, S, H, g.cnt, g.off, plan, ps);
+    group_plan_small(T, E, k, S, s_ids, g, counts, offsets, sa, ap, plan);
 }
 
-hipError_t launch_select_permute(const Shape &s, int64_t T, const float *logits, int32_t *ids,
-                                 float *w, int32_t *counts, int32_t *offsets, int32_t *sa,
-                                 int32_t *ap, const Plan &plan, hipStream_t st)
+hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, const float *Wr,
+                                const float *bias, float *logits, int32_t *ids, float *w,
+                                int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap,
+                                const Plan &plan, int *arrivals, hipStream_t st)
 {
-    select_permute_kernel<<<1, 1024, 0, st>>>((int)T, s.E, s.k, s.S, s.H, s.renorm, logits, ids,
-                                              w, counts, offsets, sa, ap, plan);
+    router_select_kernel<<<s.E, 1024, 0, st>>>((int)T, s.H, s.E, s.k, s.S, s.renorm, x, Wr, bias,
+                                               logits, ids, w, counts, offsets, sa, ap, plan, arrivals);
     return hipGetLastError();
 }
 

@@ -9,55 +9,27 @@
 namespace flint {
 
 // ---------------------------------------------------------------- decode router (T <= 32)
-// One wave per expert row: the fp32 row is read once (all 16-byte loads of a 2 KB slice in
-// flight together) and dotted against every token (x is tiny and stays in L2).  E
-// single-wave workgroups stream the whole router matrix from all CUs at once.
+// One 256-thread workgroup per expert row; wave w takes tokens w, w + 4, ...  A lane owns 8
+// consecutive h (two float4 of the fp32 row, 16 bytes of each token's bf16 x), so every
+// load is 16 bytes and all of a wave's loads for a 2048-wide slice are in flight together;
+// the row comes from HBM once per workgroup (the other waves hit in cache) and x stays in
+// L2.  Each wave reduces its tokens' sums with DPP.
 template <int MAXT>
-__global__ __launch_bounds__(64) void router_small_kernel(int T, int H, int E,
-                                                          const uint16_t *__restrict__ x,
-                                                          const float *__restrict__ Wr,
-                                                          const float *__restrict__ bias,
-                                                          float *__restrict__ logits)
+__global__ __launch_bounds__(256) void router_small_kernel(int T, int H, int E,
+                                                           const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ Wr,
+                                                           const float *__restrict__ bias,
+                                                           float *__restrict__ logits)
 {
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x;
-    float acc[MAXT];
+    constexpr int TW = (MAXT + 3) / 4;  // tokens per wave
+    const int e = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float sums[TW];
+    router_dot_wave<TW>(T, H, e, wave, 4, x, Wr, sums);
+    const float bv = bias ? bias[e] : 0.f;
 #pragma unroll
-    for (int t = 0; t < MAXT; t++) acc[t] = 0.f;
-    const float4 *w4 = reinterpret_cast<const float4 *>(Wr + (size_t)e * H);
-    constexpr int NB = 8;  // float4 loads per lane per batch (a 2048-wide slice)
-    for (int c0 = 0; c0 < H / 4; c0 += 64 * NB) {
-        float4 w[NB];
-#pragma unroll
-        for (int i = 0; i < NB; i++) {
-            const int c = c0 + 64 * i + lane;
-            w[i] = c < H / 4 ? w4[c] : float4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int t = 0; t < MAXT; t++) {
-            if (t < T) {
-                const uint16_t *xt = x + (size_t)t * H;
-#pragma unroll
-                for (int i = 0; i < NB; i++) {
-                    const int c = c0 + 64 * i + lane;
-                    if (c < H / 4) {
-                        u32x2 xv = *reinterpret_cast<const u32x2 *>(xt + 4 * c);
-                        acc[t] += bf2f(xv[0] & 0xffffu) * w[i].x;
-                        acc[t] += bf2f(xv[0] >> 16) * w[i].y;
-                        acc[t] += bf2f(xv[1] & 0xffffu) * w[i].z;
-                        acc[t] += bf2f(xv[1] >> 16) * w[i].w;
-                    }
-                }
-            }
-        }
-    }
-    const float b = bias ? bias[e] : 0.f;
-#pragma unroll
-    for (int t = 0; t < MAXT; t++) {
-        if (t < T) {
-            float s = wave_sum(acc[t]);
-            if (lane == 0) logits[(size_t)t * E + e] = s + b;
-        }
+    for (int q = 0; q < TW; q++) {
+        const int t = wave + 4 * q;
+        if (t < T && lane == 0) logits[(size_t)t * E + e] = sums[q] + bv;
     }
 }
 
@@ -172,9 +144,9 @@ hipError_t launch_router(const Shape &s, int64_t T, const uint16_t *x, const flo
                          const float *bias, float *logits, hipStream_t st)
 {
     if (T <= 8) {
-        router_small_kernel<8><<<s.E, 64, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
+        router_small_kernel<8><<<s.E, 256, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
     } else if (T <= 32) {
-        router_small_kernel<32><<<s.E, 64, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
+        router_small_kernel<32><<<s.E, 256, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
     } else {
         dim3 grid((unsigned)((T + RBM - 1) / RBM), (unsigned)((s.E + RBN - 1) / RBN));
         router_mfma_kernel<<<grid, 256, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
