@@ -244,7 +244,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return max(max(a, b), max(c, d));
 }
 
-// ---- top-k of one token (one wave) --------------------------------------------------
+// ---- top-k ---------------------------------------------------------------------------
 // Order-preserving 64-bit key: high word = monotone image of the fp32 logit (-0 mapped to
 // +0, NaN below -inf), low word = 0xffff - e so that equal logits prefer the lower index.
 __device__ __forceinline__ uint64_t select_key(float v, int e)
@@ -257,105 +257,76 @@ __device__ __forceinline__ uint64_t select_key(float v, int e)
     return ((uint64_t)ord << 32) | (uint64_t)(0xffffu - (uint32_t)e);
 }
 
-// 64-bit max as two 32-bit DPP maxima: the high words, then the low words of the lanes
-// whose high word is the maximum.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+// Four tokens per wave: the 16 lanes of DPP row g (lanes 16 g ... 16 g + 15) select for
+// token t0 + g (rows past T do nothing useful and write nothing).  Lane L of a row holds
+// experts L + 16 i (i < 16) as 32-bit keys: the order of the logit (select_key's high
+// word) plus one, 0 = no expert or already taken, so a NaN logit (order 0) still ranks
+// above those.  Each of the k rounds takes the row maximum of the keys and, among equal
+// keys, the lowest expert: every lane offers its lowest matching expert and the row
+// minimum wins.  Both reductions stay inside the row (DPP quad permutes and the half-row
+// and row mirrors), so no cross-row or scalar step is on the dependent path.  The row's
+// lane 0 writes ids[t][0..k) and the sigmoid weights (renormalised to sum 1 if renorm).
+// lg: logits of token t at lg + t * ldl.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v)
 {
-    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-    const uint32_t mh = wave_max_u32(hi);
-    const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
-    return ((uint64_t)mh << 32) | ml;
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0xB1));
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0x4E));
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0x141));
+    v = max(v, (uint32_t)FLINT_DPP((int)v, 0x140));
+    return v;
 }
-
-// Called by a whole wave.  Each lane holds experts lane, lane+64, lane+128, lane+192 as
-// 32-bit keys: the order of the logit (select_key's high word) plus one, 0 = no expert or
-// already taken, so a NaN logit (order 0) still ranks above those.  k rounds of a DPP max;
-// among equal keys the lowest expert wins: the first i with a match, the lowest lane in
-// it (ballots).  Lane 0 writes ids[0..k) and the sigmoid weights (renormalised to sum 1
-// if renorm).
-__device__ __forceinline__ void topk_token(const float *__restrict__ lg, int E, int k, int renorm,
-                                           int32_t *__restrict__ ids, float *__restrict__ wout)
+__device__ __forceinline__ uint32_t row16_min(uint32_t v)
 {
-    const int lane = threadIdx.x & 63;
-    uint32_t key[4];
+    v = min(v, (uint32_t)FLINT_DPP((int)v, 0xB1));
+    v = min(v, (uint32_t)FLINT_DPP((int)v, 0x4E));
+    v = min(v, (uint32_t)FLINT_DPP((int)v, 0x141));
+    v = min(v, (uint32_t)FLINT_DPP((int)v, 0x140));
+    return v;
+}
+__device__ __forceinline__ void topk_4tokens(const float *__restrict__ lg, int ldl, int t0, int T, int E,
+                                             int k, int renorm, int32_t *__restrict__ ids,
+                                             float *__restrict__ wout)
+{
+    const int lane = threadIdx.x & 63, g = lane >> 4, L = lane & 15, t = t0 + g;
+    const bool live = t < T;
+    const float *lt = lg + (size_t)(live ? t : t0) * ldl;
+    uint32_t key[16];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? (uint32_t)(select_key(lg[e], e) >> 32) + 1u : 0u;
+    for (int i = 0; i < 16; i++) {
+        const int e = L + 16 * i;
+        key[i] = (live && e < E) ? (uint32_t)(select_key(lt[e], e) >> 32) + 1u : 0u;
     }
-    int sel_id[8];
+    int sel[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         if (j >= k) break;
-        const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-        const uint64_t b0 = __ballot(key[0] == m), b1 = __ballot(key[1] == m);
-        const uint64_t b2 = __ballot(key[2] == m), b3 = __ballot(key[3] == m);
-        const int i = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
-        const int wl = __builtin_ctzll(b0 ? b0 : b1 ? b1 : b2 ? b2 : b3);
-        if (lane == wl) {
-            key[0] = i == 0 ? 0u : key[0];
-            key[1] = i == 1 ? 0u : key[1];
-            key[2] = i == 2 ? 0u : key[2];
-            key[3] = i == 3 ? 0u : key[3];
-        }
-        sel_id[j] = wl + 64 * i;
+        uint32_t m = key[0];
+#pragma unroll
+        for (int i = 1; i < 16; i++) m = max(m, key[i]);
+        m = row16_max(m);
+        uint32_t first = 0xffffu;  // this lane's lowest expert with key m
+#pragma unroll
+        for (int i = 15; i >= 0; i--)
+            if (key[i] == m) first = (uint32_t)(L + 16 * i);
+        const uint32_t win = row16_min(first);
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            if ((uint32_t)(L + 16 * i) == win) key[i] = 0u;
+        sel[j] = (int)win;
     }
-    if (lane == 0) {
+    if (live && L == 0) {
         float sg[8];
         float sum = 0.f;
         for (int j = 0; j < k; j++) {
-            sg[j] = 1.0f / (1.0f + expf(-lg[sel_id[j]]));
+            sg[j] = 1.0f / (1.0f + expf(-lt[sel[j]]));
             sum += sg[j];
         }
         for (int j = 0; j < k; j++) {
-            ids[j] = sel_id[j];
-            wout[j] = renorm ? sg[j] / sum : sg[j];
+            ids[(size_t)t * k + j] = sel[j];
+            wout[(size_t)t * k + j] = renorm ? sg[j] / sum : sg[j];
         }
     }
 }
 
-// ---- grouping of at most 64 assignments by one wave ---------------------------------
-// ids[a] (a < n <= 64) are expert ids.  Computes, in the order of a stable sort by expert:
-// slot_of[a] (position of a), and the touched-expert list (ascending id, then the shared
-// expert E with all T tokens when S): touched[u], tbase[u] (first slot), tcount[u].
-// Returns the list length (wave-uniform).
-__device__ __forceinline__ int wave_group_small(int n, int T, int k, int E, int S,
-                                                const int32_t *ids, int *touched, int *tbase,
-                                                int *tcount, int *slot_of)
-{
-    const int lane = threadIdx.x & 63;
-    const bool valid = lane < n;
-    const int e = valid ? ids[lane] : 0x7fffffff;
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 9; b++) {
-        const bool bit = valid && ((e >> b) & 1);
-        const uint64_t vote = __ballot(bit);
-        peers &= bit ? vote : ~vote;
-    }
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank = __popcll(peers & lt), size = __popcll(peers);
-    const bool leader = valid && rank == 0;
-    const uint64_t lmask = __ballot(leader);
-    int below = 0, lead_below = 0;
-    for (int j = 0; j < n; j++) {
-        const int ej = __builtin_amdgcn_readlane(e, j);
-        below += (ej < e);
-        lead_below += (int)((lmask >> j) & 1ull) & (int)(ej < e);
-    }
-    if (valid) slot_of[lane] = below + rank;
-    if (leader) {
-        touched[lead_below] = e;
-        tbase[lead_below] = below;
-        tcount[lead_below] = size;
-    }
-    const int nr = __popcll(lmask);
-    if (S && lane == 0) {
-        touched[nr] = E;
-        tbase[nr] = T * k;
-        tcount[nr] = T;
-    }
-    return nr + S;
-}
 
 }  // namespace flint

@@ -209,8 +209,8 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
 // wave w takes tokens w and w + 16) computes the logits of expert e and writes them with
 // agent-scope write-through stores; once they have completed it counts itself in at an
 // agent-scope arrival counter.  The workgroup that arrives last has every logit: it reads
-// them back with agent-scope loads into LDS, selects the top-k of every token (one wave
-// per token), groups the assignments by expert and writes the plan, so the expert
+// them back with agent-scope loads into LDS, selects the top-k of every token (four
+// tokens per wave), groups the assignments by expert and writes the plan, so the expert
 // kernels that follow need no routing step of their own.  It also re-arms the counter.
 __global__ __launch_bounds__(1024) void router_select_kernel(
     int T, int H, int E, int k, int S, int renorm, const uint16_t *__restrict__ x,
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(1024) void router_select_kernel(
         s_lg[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(arrivals, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    for (int t = wv; t < T; t += 16) topk_token(s_lg + t * E, E, k, renorm, s_ids + t * k, s_w + t * k);
+    if (4 * wv < T) topk_4tokens(s_lg, E, 4 * wv, T, E, k, renorm, s_ids, s_w);  // 4 tokens per wave
     __syncthreads();
     for (int a = tid; a < T * k; a += 1024) {
         ids[a] = s_ids[a];

@@ -155,22 +155,21 @@ hipError_t launch_router(const Shape &s, int64_t T, const uint16_t *x, const flo
 }
 
 // ---------------------------------------------------------------- top-k select
-// One wave per token; each lane holds experts lane, lane+64, lane+128, lane+192.
-// k rounds of a wave-wide arg-max; the winning lane retires its entry.
+// Four tokens per wave (16 lanes each), four waves per workgroup.
 __global__ __launch_bounds__(256) void topk_kernel(int T, int E, int k, int renorm,
                                                    const float *__restrict__ logits,
                                                    int32_t *__restrict__ ids,
                                                    float *__restrict__ wout)
 {
-    const int t = blockIdx.x * 4 + threadIdx.x / 64;
-    if (t >= T) return;
-    topk_token(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wout + (size_t)t * k);
+    const int t0 = blockIdx.x * 16 + (threadIdx.x >> 6) * 4;
+    if (t0 >= T) return;
+    topk_4tokens(logits, E, t0, T, E, k, renorm, ids, wout);
 }
 
 hipError_t launch_topk(const Shape &s, int64_t T, const float *logits, int32_t *ids, float *w,
                        hipStream_t st)
 {
-    unsigned blocks = (unsigned)((T + 3) / 4);
+    unsigned blocks = (unsigned)((T + 15) / 16);
     topk_kernel<<<blocks, 256, 0, st>>>((int)T, s.E, s.k, s.renorm, logits, ids, w);
     return hipGetLastError();
 }
