@@ -243,7 +243,7 @@ static int forward_impl(const Shape &s, const WSet &wset, int64_t T, const uint1
     char *b = (char *)ws;
     if (T <= kGemvMaxT) {
         return hip_status(launch_gemv_forward(s, wset, T, x, topk_w, sa, ap, plan,
-                                              (uint16_t *)(b + L.h), y, st));
+                                              (uint16_t *)(b + L.h), (float *)(b + L.o), y, st));
     }
     return hip_status(launch_gemm_forward(s, wset, T, x, topk_w, sa, ap, plan,
                                           (uint16_t *)(b + L.h), (uint16_t *)(b + L.o), y, st));

@@ -91,7 +91,7 @@ hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, cons
 // Streaming path (T <= kGemvMaxT) from an existing plan.
 hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
-                               const Plan &plan, uint16_t *h, uint16_t *y, hipStream_t st);
+                               const Plan &plan, uint16_t *h, float *o, uint16_t *y, hipStream_t st);
 hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                                const float *topk_w, const int32_t *sa, const int32_t *ap,
                                const Plan &plan, uint16_t *h, uint16_t *o, uint16_t *y,
