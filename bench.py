@@ -11,7 +11,8 @@ HIP graph.  Inputs are seeded synthetic data drawn on the device before timing.
 Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant kernel (bytes or
 flops per launch over its measured duration) and the reference's single-core CPU rate on
 a bounded sample.  --config picks another workload: decode_t8, decode_t32, prefill,
-prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32.
+prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32, nvfp4_prefill, and the dense SwiGLU layer
+(no router, I = 4096) at dense_t1, dense_t32, dense_prefill.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 H, I, E, TOPK, S = 2048, 768, 256, 6, 1
+DENSE_I = 4096  # intermediate size of the dense SwiGLU layers (not given by the pages)
 CONFIGS = {
     "decode_t1": dict(T=1, fmt=0, layers=47, zipf=False),
     "decode_t8": dict(T=8, fmt=0, layers=47, zipf=False),
@@ -36,13 +38,28 @@ CONFIGS = {
     "nvfp4_t1": dict(T=1, fmt=1, layers=47, zipf=False),
     "nvfp4_t8": dict(T=8, fmt=1, layers=47, zipf=False),
     "nvfp4_t32": dict(T=32, fmt=1, layers=47, zipf=False),
+    "nvfp4_prefill": dict(T=8192, fmt=1, layers=1, zipf=False),
+    # dense SwiGLU layers (E = 0, k = 0, the shared expert alone; 16 distinct layers cycled)
+    "dense_t1": dict(T=1, fmt=0, layers=16, zipf=False, dense=True),
+    "dense_t32": dict(T=32, fmt=0, layers=16, zipf=False, dense=True),
+    "dense_prefill": dict(T=8192, fmt=0, layers=1, zipf=False, dense=True),
 }
+
+
+def shape_of(cfg):
+    """(H, I, E, k, S) of a workload."""
+    if cfg.get("dense"):
+        return H, DENSE_I, 0, 0, 1
+    return H, I, E, TOPK, S
+
+
+def expert_bytes(fmt, H_, I_):
+    return 3 * I_ * H_ * 2 if fmt == 0 else 3 * (I_ * H_ // 2 + I_ * H_ // 16) + 3 * 4
 METRIC = "MoE-layer tokens/s at T=1/8/32/8192; achieved HBM GB/s or MFMA % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "sparse_moe_transformer_wave_amd", "csrc")
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-EXPERT_BYTES = {0: 3 * I * H * 2, 1: 3 * (I * H // 2 + I * H // 16) + 3 * 4}
 
 
 def log(msg):
@@ -87,21 +104,27 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
-def build_layer(torch, fm, dg, l, fmt, zipf):
+def build_layer(torch, fm, dg, l, fmt, zipf, shp):
     """Layer l of the seeded pool, drawn on the device."""
-    d = {}
-    d["Wr"] = torch.empty((E, H), dtype=torch.float32, device="cuda")
-    dg.device_normal_f32(d["Wr"], 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
-    d["bias"] = torch.from_numpy(dg.zipf_bias(E, dg.ZIPF_C, 0, l)).cuda() if zipf else None
+    H, I, E, _, S = shp
+    d = {"Wr": None, "bias": None}
+    if E:
+        d["Wr"] = torch.empty((E, H), dtype=torch.float32, device="cuda")
+        dg.device_normal_f32(d["Wr"], 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+        d["bias"] = torch.from_numpy(dg.zipf_bias(E, dg.ZIPF_C, 0, l)).cuda() if zipf else None
     kinds = (("gate", dg.KIND_GATE, I, H), ("up", dg.KIND_UP, I, H), ("down", dg.KIND_DOWN, H, I))
     if fmt == 0:
         for name, kind, N, K in kinds:
             t = torch.empty((E + S, N, K), dtype=torch.int16, device="cuda")
             dg.device_normal_bf16(t, E + S, N * K, 0, dg.stream_id(l, kind, 0), dg.W_STD)
             d[name] = t
-        d["weights"] = fm.Weights(0, d["gate"], d["up"], d["down"], d["gate"][E], d["up"][E],
-                                  d["down"][E])
+        if E == 0:  # dense layer: the shared expert's pointers only
+            d["weights"] = fm.Weights(0, None, None, None, d["gate"][0], d["up"][0], d["down"][0])
+        else:
+            d["weights"] = fm.Weights(0, d["gate"], d["up"], d["down"], d["gate"][E], d["up"][E],
+                                      d["down"][E])
     else:
+        assert E > 0, "dense NVFP4 layers are not part of the benchmark"
         scratch = torch.empty(E + S, dtype=torch.int32, device="cuda")
         for name, kind, N, K in kinds:
             q = torch.empty((E + S, N, K // 2), dtype=torch.uint8, device="cuda")
@@ -127,10 +150,15 @@ def cpu_baseline(cfg, budget_s):
 
     import oracle
     from sparse_moe_transformer_wave_amd import datagen as dg
-    T = cfg["T"] if cfg["T"] <= 32 else 4
-    n_layers = min(8, cfg["layers"])
+    H, I, E, TOPK, S = shape_of(cfg)
+    nvfp4 = cfg["fmt"] == 1
+    # host quantisation costs ~1 s per expert: NVFP4 samples 2 tokens of one layer
+    T = min(cfg["T"], 2) if nvfp4 else cfg["T"] if cfg["T"] <= 32 else 4
+    n_layers = min(1 if nvfp4 else 8, cfg["layers"])
     x = dg.normal_bf16((cfg["T"], H), 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)[:T]
     x = np.ascontiguousarray(x)
+    if E == 0:
+        return cpu_baseline_dense(cfg, budget_s, x, H, I, n_layers)
     layers = []
     for l in range(n_layers):
         Wr = dg.normal_f32((E, H), 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
@@ -138,13 +166,19 @@ def cpu_baseline(cfg, budget_s):
         ids = oracle.select(oracle.router(x, Wr, bias), TOPK)
         used = sorted(set(ids.reshape(-1).tolist()))
         local = {e: i for i, e in enumerate(used)}
-        arrays = {"gate": [], "up": [], "down": []}
+        arrays = {}
         for e in used + [E]:
             for name, kind, shape in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
                                       ("down", dg.KIND_DOWN, (H, I))):
-                arrays[name].append(dg.normal_bf16(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
-        routed = oracle.Experts(oracle.FMT_BF16, H, I, {k: np.stack(v[:-1]) for k, v in arrays.items()})
-        shared = oracle.Experts(oracle.FMT_BF16, H, I, {k: np.stack(v[-1:]) for k, v in arrays.items()})
+                if nvfp4:
+                    q, sb, st = oracle.nvfp4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
+                    for pre, v in (("q_", q), ("sb_", sb), ("st_", np.float32(st))):
+                        arrays.setdefault(pre + name, []).append(v)
+                else:
+                    arrays.setdefault(name, []).append(dg.normal_bf16(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
+        fmt_o = oracle.FMT_NVFP4 if nvfp4 else oracle.FMT_BF16
+        routed = oracle.Experts(fmt_o, H, I, {k: np.stack(v[:-1]) for k, v in arrays.items()})
+        shared = oracle.Experts(fmt_o, H, I, {k: np.stack(v[-1:]) for k, v in arrays.items()})
         layers.append((Wr, bias, local, routed, shared))
     done, t_used = 0, 0.0
     while t_used < budget_s:
@@ -157,6 +191,10 @@ def cpu_baseline(cfg, budget_s):
         oracle.moe_tokens(routed, shared, x, lid, w)
         t_used += time.perf_counter() - t0
         done += 1
+    return cpu_result(T, done, n_layers, t_used, "full layer, NVFP4 weights" if nvfp4 else "full layer")
+
+
+def host_cpu():
     cpu = platform.processor() or platform.machine()
     try:
         for line in open("/proc/cpuinfo"):
@@ -165,10 +203,38 @@ def cpu_baseline(cfg, budget_s):
                 break
     except OSError:
         pass
+    return cpu
+
+
+def cpu_result(T, done, n_layers, t_used, what):
     return {"value": T * done / t_used, "unit": "MoE-layer tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d token(s) x %d layer evaluations (layers 0..%d cycled), full layer, "
+            "sample": "%d token(s) x %d layer evaluations (layers 0..%d cycled), %s, "
                       "single-threaded fp64 C reference, %.1f s; host CPU %s, %d logical cores"
-                      % (T, done, n_layers - 1, t_used, cpu, os.cpu_count() or 0)}
+                      % (T, done, n_layers - 1, what, t_used, host_cpu(), os.cpu_count() or 0)}
+
+
+def cpu_baseline_dense(cfg, budget_s, x, H, I, n_layers):
+    """The reference's SwiGLU expert (the dense layer) for each token, layers cycled."""
+    import numpy as np
+
+    import oracle
+    from sparse_moe_transformer_wave_amd import datagen as dg
+    layers = []
+    for l in range(n_layers):
+        arrays = {name: dg.normal_bf16(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD)[None]
+                  for name, kind, shape in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
+                                            ("down", dg.KIND_DOWN, (H, I)))}
+        layers.append(oracle.Experts(oracle.FMT_BF16, H, I, arrays))
+    xf = dg.bf16_bits_to_f32(x).astype(np.float64)
+    done, t_used = 0, 0.0
+    while t_used < budget_s:
+        ex = layers[done % n_layers]
+        t0 = time.perf_counter()
+        for t in range(x.shape[0]):
+            oracle.expert_ffn(ex, 0, xf[t])
+        t_used += time.perf_counter() - t0
+        done += 1
+    return cpu_result(x.shape[0], done, n_layers, t_used, "dense SwiGLU layer")
 
 
 def main():
@@ -198,26 +264,34 @@ def main():
 
     cfg = CONFIGS[args.config]
     T, fmt, L = cfg["T"], cfg["fmt"], cfg["layers"]
+    shp = shape_of(cfg)
+    H, I, E, TOPK, S = shp
     torch.cuda.init()
     log("config %s: T=%d fmt=%s layers=%d" % (args.config, T, "bf16" if fmt == 0 else "nvfp4", L))
     t0 = time.time()
-    layers = [build_layer(torch, fm, dg, l, fmt, cfg["zipf"]) for l in range(L)]
+    layers = [build_layer(torch, fm, dg, l, fmt, cfg["zipf"], shp) for l in range(L)]
     x = torch.empty((T, H), dtype=torch.int16, device="cuda")
     dg.device_normal_bf16(x, 1, T * H, 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     desc = fm.desc(H, I, E, TOPK, S, 1)
     ws = fm.workspace(desc, T, fmt)
     torch.cuda.synchronize()
+    xb = expert_bytes(fmt, H, I)
     log("pool ready (%.1f GB of expert weights) in %.1f s"
-        % (L * (E + S) * EXPERT_BYTES[fmt] / 1e9, time.time() - t0))
+        % (L * (E + S) * xb / 1e9, time.time() - t0))
 
     # Routing of every layer (for the algorithmic byte count: distinct experts touched).
-    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
     touched = []
-    for d in layers:
-        fm.layer(desc, d["weights"], T, x, d["Wr"], d["bias"], y, ws, {"counts": counts})
-        touched.append(int((counts > 0).sum().item()))
-    alg_bytes = [(u + S) * EXPERT_BYTES[fmt] + E * H * 4 + 4 * T * H for u in touched]
+    if E:
+        counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+        for d in layers:
+            fm.layer(desc, d["weights"], T, x, d["Wr"], d["bias"], y, ws, {"counts": counts})
+            touched.append(int((counts > 0).sum().item()))
+    else:
+        for d in layers:
+            fm.layer(desc, d["weights"], T, x, None, None, y, ws)
+            touched.append(0)
+    alg_bytes = [(u + S) * xb + E * H * 4 + 4 * T * H for u in touched]
     flops_layer = 2.0 * T * (TOPK + S) * 3 * H * I
 
     stream = torch.cuda.current_stream()
@@ -278,8 +352,9 @@ def main():
         achieved = bytes_per_call / (avg_call_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
-                "kernel": ("decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
-                           "flint_moe_layer (router + fused select/gate-up + down kernels)"),
+                "kernel": ("flint_moe_layer (dense: plan, gate/up, down, combine kernels)" if E == 0 else
+                           "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
+                           "flint_moe_layer (router with selection, gate/up, down, combine kernels)"),
                 "avg_launch_us": round(avg_call_ms * 1e3, 2),
                 "alg_bytes_per_launch": int(bytes_per_call)}
     else:
@@ -295,10 +370,13 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if fmt == 0 else "nvfp4-w4a16 (e2m1 weights x bf16 activations, fp32 accumulate)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tokens, drawn on device)",
-        "config": {"workload": "%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, "
-                               "SwiGLU, %s, %d distinct layers cycled%s"
-                               % (args.config, T, H, I, E, TOPK, S, "bf16" if fmt == 0 else "NVFP4",
-                                  L, ", Zipf(1.1) logit bias" if cfg["zipf"] else ""),
+        "config": {"workload": ("%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, "
+                                "SwiGLU, %s, %d distinct layers cycled%s"
+                                % (args.config, T, H, I, E, TOPK, S, "bf16" if fmt == 0 else "NVFP4",
+                                   L, ", Zipf(1.1) logit bias" if cfg["zipf"] else "")) if E else
+                               ("%s: T=%d tokens, dense SwiGLU FFN layer (no router), H=%d, I=%d, "
+                                "%s, %d distinct layers cycled" % (args.config, T, H, I,
+                                                                   "bf16" if fmt == 0 else "NVFP4", L)),
                    "tokens_per_layer_call": T, "layers": L, "touched_experts_mean": float(np.mean(touched))},
         "roofline": roof,
     }

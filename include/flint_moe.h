@@ -24,6 +24,15 @@
  *   - Supported shapes: 1 <= E <= 256; 1 <= k <= min(8, E); n_shared in {0, 1};
  *     hidden % 256 == 0 and 256 <= hidden <= 8192; inter % 128 == 0 and
  *     128 <= inter <= 4096; 0 <= T <= 65536.  Every pointer must be 16-byte aligned.
+ *   - Dense layers: E == 0 with k == 0 and n_shared == 1 describes a dense SwiGLU FFN
+ *     (the Flint model has 2 dense layers beside its 47 MoE layers: neoteo.com
+ *     specification table, row "Warstwy"; their intermediate size is not given, so
+ *     it is `inter`):
+ *     y = bf16(down(silu(gate x) * up x)) with the sh_* weights, no router and no
+ *     routing.  flint_moe_forward and flint_moe_layer accept it (routing arguments,
+ *     w_router and logit_bias unused and may be NULL; the routed weight pointers and
+ *     their scales must be NULL); flint_moe_route and flint_moe_permute return
+ *     FLINT_ERR_SHAPE.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
  *   - A workspace's first 80 KiB hold the single-token path's launch counter, error flag
  *     and exchange words: zero them once before first use (flint_moe_workspace_init, or
@@ -164,7 +173,8 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
    routing tensors the caller asks for.  A single token (T == 1) runs as one persistent
    launch of one workgroup per CU (on a device with at least 256 CUs) whose workgroups
    exchange logits and h through tagged words at the start of the workspace (see
-   flint_moe_workspace_init); it keeps h and the per-slot outputs in fp32.  A wait there
+   flint_moe_workspace_init); it rounds h to bf16 like the other paths and combines the
+   per-slot outputs in fp32.  A wait there
    that runs out (it cannot on a device with a CU per workgroup) sets the word at byte 4
    of the workspace to 1. */
 int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,

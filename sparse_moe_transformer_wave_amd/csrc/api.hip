@@ -22,9 +22,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 int check_desc(const flint_moe_desc *d)
 {
     if (!d) return FLINT_ERR_NULL;
-    if (d->n_experts < 1 || d->n_experts > 256) return FLINT_ERR_SHAPE;
-    if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts) return FLINT_ERR_SHAPE;
-    if (d->n_shared != 0 && d->n_shared != 1) return FLINT_ERR_SHAPE;
+    if (d->n_experts == 0) {  // dense SwiGLU layer: the shared expert alone, no routing
+        if (d->top_k != 0 || d->n_shared != 1) return FLINT_ERR_SHAPE;
+    } else {
+        if (d->n_experts < 1 || d->n_experts > 256) return FLINT_ERR_SHAPE;
+        if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts) return FLINT_ERR_SHAPE;
+        if (d->n_shared != 0 && d->n_shared != 1) return FLINT_ERR_SHAPE;
+    }
     if (d->hidden < 256 || d->hidden > 8192 || d->hidden % 256) return FLINT_ERR_SHAPE;
     if (d->inter < 128 || d->inter > 4096 || d->inter % 128) return FLINT_ERR_SHAPE;
     if (d->renormalize != 0 && d->renormalize != 1) return FLINT_ERR_SHAPE;
@@ -47,7 +51,15 @@ int check_weights(const flint_moe_desc *d, const flint_moe_weights *w)
 {
     if (!w) return FLINT_ERR_NULL;
     if (w->format != FLINT_WFMT_BF16 && w->format != FLINT_WFMT_NVFP4) return FLINT_ERR_FORMAT;
-    if (!w->gate || !w->up || !w->down) return FLINT_ERR_NULL;
+    const bool dense = d->n_experts == 0;
+    if (dense) {  // no routed experts: their pointers must be NULL
+        const void *rp[] = {w->gate, w->up, w->down, w->gate_sf, w->up_sf, w->down_sf,
+                            w->gate_ts, w->up_ts, w->down_ts};
+        for (const void *p : rp)
+            if (p) return FLINT_ERR_FORMAT;
+    } else if (!w->gate || !w->up || !w->down) {
+        return FLINT_ERR_NULL;
+    }
     const bool has_sh = w->sh_gate && w->sh_up && w->sh_down;
     const bool any_sh = w->sh_gate || w->sh_up || w->sh_down;
     if (d->n_shared && !has_sh) return FLINT_ERR_NULL;
@@ -64,7 +76,7 @@ int check_weights(const flint_moe_desc *d, const flint_moe_weights *w)
             if (p) return FLINT_ERR_FORMAT;
     } else {
         for (const void *p : sc)
-            if (!p) return FLINT_ERR_FORMAT;
+            if (!dense && !p) return FLINT_ERR_FORMAT;
         for (const void *p : sc)
             if (!aligned16(p)) return FLINT_ERR_ALIGN;
         for (const void *p : shsc) {
@@ -190,7 +202,7 @@ int flint_moe_route(const flint_moe_desc *desc, int64_t T, const uint16_t *x,
 {
     int rc = check_desc(desc);
     if (rc) return rc;
-    if (T < 0 || T > kMaxT) return FLINT_ERR_SHAPE;
+    if (desc->n_experts == 0 || T < 0 || T > kMaxT) return FLINT_ERR_SHAPE;
     if (flags & ~(uint32_t)FLINT_ROUTE_LOGITS_IN) return FLINT_ERR_FORMAT;
     if (T == 0) return FLINT_OK;
     const bool lin = flags & FLINT_ROUTE_LOGITS_IN;
@@ -222,7 +234,7 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
 {
     int rc = check_desc(desc);
     if (rc) return rc;
-    if (T < 0 || T > kMaxT) return FLINT_ERR_SHAPE;
+    if (desc->n_experts == 0 || T < 0 || T > kMaxT) return FLINT_ERR_SHAPE;
     if (T == 0) return FLINT_OK;
     if (!topk_ids || !counts || !offsets || !sorted_assign || !assign_pos) return FLINT_ERR_NULL;
     const void *ptrs[] = {topk_ids, counts, offsets, sorted_assign, assign_pos};
@@ -262,7 +274,9 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
     rc = check_weights(desc, weights);
     if (rc) return rc;
     if (T == 0) return FLINT_OK;
-    if (!x || !topk_ids || !topk_w || !offsets || !sorted_assign || !assign_pos || !y || !ws)
+    const bool dense = desc->n_experts == 0;  // routing arguments unused (may be NULL)
+    if (!x || !y || !ws) return FLINT_ERR_NULL;
+    if (!dense && (!topk_ids || !topk_w || !offsets || !sorted_assign || !assign_pos))
         return FLINT_ERR_NULL;
     const void *ptrs[] = {x, topk_ids, topk_w, offsets, sorted_assign, assign_pos, y, ws};
     for (const void *p : ptrs)
@@ -272,7 +286,7 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
     if (ws_bytes < L.total) return FLINT_ERR_WORKSPACE;
     const Plan plan = plan_view(ws, L, s);
     hipStream_t st = (hipStream_t)stream;
-    rc = hip_status(launch_plan(s, T, offsets, plan, st));
+    rc = hip_status(launch_plan(s, T, dense ? nullptr : offsets, plan, st));
     if (rc) return rc;
     return forward_impl(s, wset_of(weights), T, x, topk_w, sorted_assign, assign_pos, y, ws, L,
                         plan, st);
@@ -289,7 +303,8 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     rc = check_weights(desc, weights);
     if (rc) return rc;
     if (T == 0) return FLINT_OK;
-    if (!x || !w_router || !y || !ws) return FLINT_ERR_NULL;
+    const bool dense = desc->n_experts == 0;  // no router: w_router, logit_bias, routing unused
+    if (!x || (!dense && !w_router) || !y || !ws) return FLINT_ERR_NULL;
     const void *ptrs[] = {x, w_router, logit_bias, y, ws};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FLINT_ERR_ALIGN;
@@ -312,6 +327,11 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     int32_t *ap = R.assign_pos ? R.assign_pos : (int32_t *)(b + L.ap);
     hipStream_t st = (hipStream_t)stream;
     const Plan plan = plan_view(ws, L, s);
+    if (dense) {
+        rc = hip_status(launch_plan(s, T, nullptr, plan, st));
+        if (rc) return rc;
+        return forward_impl(s, wset_of(weights), T, x, nullptr, nullptr, nullptr, y, ws, L, plan, st);
+    }
     if (T == 1 && decode1_supported(s, weights->format)) {
         return hip_status(launch_decode1(s, wset_of(weights), x, w_router, logit_bias, y, lg, ids, tw,
                                          cnt, off, sa, ap, b + L.sync, st));

@@ -514,7 +514,7 @@ bool decode1_supported(const Shape &s, int fmt)
 {
     const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + s.I / 16;
     const int rows_h = s.H / kG;
-    return s.H % kG == 0 && s.H <= 2048 &&                   // rows_h <= 8, x in 4 chunks per lane
+    return s.E >= 1 && s.H % kG == 0 && s.H <= 2048 &&                   // rows_h <= 8, x in 4 chunks per lane
            s.I % 32 == 0 && s.I <= 1024 && s.k <= kMaxK &&    // <= 4 gate/up pairs: one row per wave
            (size_t)rows_h * row % 16 == 0 &&                  // whole 16-byte chunks per block
            d1_dyn_bytes(s, fmt) + sizeof(D1Shared) <= 160 * 1024 && device_cus() >= kG;

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 #pragma unroll
     for (int mt = 0; mt < NMT; mt++) {
         const int idx = min(mt * 16 + r, cnt - 1);
-        tix[mt] = (e == E) ? idx * k : sa_in[base + idx];  // assignment index; token = tix / k
+        tix[mt] = (e == E) ? idx : sa_in[base + idx] / k;  // token of the A row (k >= 1 if routed)
     }
     const uint16_t *xr[NMT];
     const int nmt = (cnt + 15) >> 4;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 #pragma unroll
                 for (int i = 0; i < NB; i++) b[q][i] = ld16(W0 + (size_t)q * 8 * H + kq + i * 32);
 #pragma unroll
-        for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)(tix[mt] / k) * H;
+        for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)tix[mt] * H;
         for (; c0 + NB <= cpw; c0 += NB) {   // full batches: every load issued, no branches
             u32x4 a[NMT][NB];
             if (c0 > 0)
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
         const uint8_t *Q0 = expert_base(wm, e, E, (size_t)I * H / 2) + (size_t)(i0 + (r & 7)) * (H / 2);
         const uint8_t *SF0 = expert_sf(wm, e, E, (size_t)I * H / 16) + (size_t)(i0 + (r & 7)) * (H / 16);
 #pragma unroll
-        for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)(tix[mt] / k) * H;
+        for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)tix[mt] * H;
         const int nsc = H / 128;
         constexpr int NB = 4;
         for (int s0 = wave; s0 < nsc; s0 += 4 * NB) {
@@ -202,22 +202,28 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 }
 
 // ------------------------------------------------------------------ pass 2: down
-// One workgroup per (touched expert, 64 rows of H): wave w multiplies rows 64 nb + 16 w ...
-// + 15 (MFMA columns) over all of K = I against the expert's h rows, every load of a batch
-// in flight; per-slot outputs o[slot][n] go to the workspace in fp32.  `cls` as for gate/up.  Thousands of small
-// independent workgroups keep the weight stream busy the way the gate/up pass does.
-template <int FMT, int NMT>
+// KS = 1: one workgroup per (touched expert, 64 rows of H): wave w multiplies rows 64 nb +
+// 16 w ... + 15 (MFMA columns) over all of K = I against the expert's h rows, every load of
+// a batch in flight.  KS = 4 (few experts, e.g. a dense layer): one workgroup per (expert,
+// 16 rows), wave w takes the w-th quarter of K and the quarters are summed through LDS, so
+// four times as many waves stream the same rows.  Per-slot outputs o[slot][n] go to the
+// workspace in fp32.  `cls` as for gate/up.  Thousands of small independent workgroups
+// keep the weight stream busy the way the gate/up pass does.
+template <int FMT, int NMT, int KS>
 __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int cls, WSet w,
                                                         const uint16_t *__restrict__ h, Plan p,
                                                         float *__restrict__ o)
 {
-    const int nrb = H / 64;
+    static_assert(KS == 1 || KS == 4, "K split over the 4 waves or none");
+    __shared__ f32x4 red[KS == 4 ? 3 : 1][NMT][64];
+    const int nrb = H / (64 / KS);
     const int u = blockIdx.x / nrb, nb = blockIdx.x - u * nrb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int nT = p.meta[0];
     const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
     if (u >= nT || (cls == 1 && cnt > 16) || (cls == 2 && cnt <= 16)) return;
-    const int row = nb * 64 + wave * 16 + r;  // MFMA column r of this wave
+    const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * 16 + r;  // MFMA column r of this wave
+    const int kw = KS == 1 ? 0 : wave;  // this wave's part of K
     const int nmt = (cnt + 15) >> 4;
     const uint16_t *hr[NMT];
     bool has_tok[NMT];  // this lane's A row is one of the expert's tokens
@@ -233,10 +239,10 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
     if (FMT == 0) {
         const uint16_t *Wd = reinterpret_cast<const uint16_t *>(expert_base(w.down, e, E, (size_t)H * I * 2)) +
                              (size_t)row * I;
-        const int nch = I / 32;
-        constexpr int NB = NMT == 1 ? 24 : 12;
-        int c0 = 0;
-        for (; c0 + NB <= nch; c0 += NB) {   // full batches: every load issued, no branches
+        const int nch = I / 32, ce = nch * (kw + 1) / KS;
+        constexpr int NB = (NMT == 1 ? 24 : 12) / KS;
+        int c0 = nch * kw / KS;
+        for (; c0 + NB <= ce; c0 += NB) {   // full batches: every load issued, no branches
             u32x4 b[NB], a[NMT][NB];
 #pragma unroll
             for (int i = 0; i < NB; i++) b[i] = ld16(Wd + (c0 + i) * 32 + g * 8);
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                 for (int mt = 0; mt < NMT; mt++)
                     if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i]), as_bf16x8(b[i]), acc[mt]);
         }
-        for (; c0 < nch; c0++) {               // tail
+        for (; c0 < ce; c0++) {                // tail
             const u32x4 b = ld16(Wd + c0 * 32 + g * 8);
 #pragma unroll
             for (int mt = 0; mt < NMT; mt++)
@@ -262,16 +268,16 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
         const uint8_t *Qd = expert_base(w.down, e, E, (size_t)H * I / 2) + (size_t)row * (I / 2);
         const uint8_t *Sd = expert_sf(w.down, e, E, (size_t)H * I / 16) + (size_t)row * (I / 16);
         ts = expert_ts(w.down, e, E);
-        const int nsc = I / 128;
-        constexpr int NB = NMT == 1 ? 6 : 3;
-        for (int s0 = 0; s0 < nsc; s0 += NB) {
+        const int nsc = I / 128, se = nsc * (kw + 1) / KS;
+        constexpr int NB = KS == 1 ? (NMT == 1 ? 6 : 3) : 2;
+        for (int s0 = nsc * kw / KS; s0 < se; s0 += NB) {
             u32x4 q[NB], a[NMT][NB][4];
             uint32_t sb[NB];
 #pragma unroll
             for (int i = 0; i < NB; i++) {
                 q[i] = u32x4{0u, 0u, 0u, 0u};
                 sb[i] = 0u;
-                if (s0 + i < nsc) {
+                if (s0 + i < se) {
                     const int kb = (s0 + i) * 128 + g * 32;
                     q[i] = ld16(Qd + kb / 2);
                     sb[i] = *reinterpret_cast<const uint16_t *>(Sd + kb / 16);
@@ -282,13 +288,13 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                 if (NMT == 1 || mt < nmt)
 #pragma unroll
                     for (int i = 0; i < NB; i++)
-                        if (s0 + i < nsc)
+                        if (s0 + i < se)
 #pragma unroll
                             for (int j = 0; j < 4; j++)
                                 a[mt][i][j] = has_tok[mt] ? ld16(hr[mt] + (s0 + i) * 128 + g * 32 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < NB; i++) {
-                if (s0 + i < nsc) {
+                if (s0 + i < se) {
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
                         bf16x8 bv = as_bf16x8(dequant8(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
@@ -299,6 +305,20 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                 }
             }
         }
+    }
+    if (KS == 4) {  // waves 1..3 hand their partial sums to wave 0 (K order: wave 0 first)
+        if (wave > 0)
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) red[KS == 4 ? wave - 1 : 0][mt][lane] = acc[mt];
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int q = 0; q < 3; q++)
+#pragma unroll
+            for (int mt = 0; mt < NMT; mt++) {
+                const f32x4 v = red[KS == 4 ? q : 0][mt][lane];
+                acc[mt] = f32x4{acc[mt][0] + v[0], acc[mt][1] + v[1], acc[mt][2] + v[2], acc[mt][3] + v[3]};
+            }
     }
     // D[m][n]: lane 16 (m / 4) + n, element m % 4; rows (slots) of this lane: m = 4 g + i.
 #pragma unroll
@@ -373,11 +393,15 @@ static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, in
     gemv_gateup_kernel<FMT, NMT, RG><<<grid, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, w, x, sa, plan, h);
 }
 
+// Split K over the waves when 64-row workgroups would leave most CUs idle.
 template <int FMT, int NMT>
 static void launch_down(const Shape &s, const WSet &w, int maxU, int cls, const uint16_t *h,
                         const Plan &plan, float *o, hipStream_t st)
 {
-    gemv_down_kernel<FMT, NMT><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, cls, w, h, plan, o);
+    if (maxU * (s.H / 64) >= 512)
+        gemv_down_kernel<FMT, NMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, cls, w, h, plan, o);
+    else
+        gemv_down_kernel<FMT, NMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, cls, w, h, plan, o);
 }
 
 // T <= 16: every unit fits one token tile.  Larger T: units of at most 16 tokens (all but

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void plan_kernel(int T, int E, int k, int S, i
     __shared__ int cnt[256];
     __shared__ int off[257];
     __shared__ PlanScratch ps;
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) off[e] = offsets[e];
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) off[e] = E ? offsets[e] : 0;  // E = 0: dense
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = off[e + 1] - off[e];
     __syncthreads();

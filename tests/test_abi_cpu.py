@@ -109,3 +109,32 @@ def test_forward_and_layer_validation():
     assert L.flint_moe_layer(ctypes.byref(d), ctypes.byref(w), 4, A, A, None, A, None, A, 16, None) == fm.ERR_WORKSPACE
     assert L.flint_moe_permute(ctypes.byref(d), 4, A, A, None, A, A, None, 0, None) == fm.ERR_NULL
     assert L.flint_moe_permute(ctypes.byref(d), 0, None, None, None, None, None, None, 0, None) == fm.OK
+
+
+def test_dense_layer_validation():
+    """n_experts = 0, top_k = 0, n_shared = 1 is a dense SwiGLU layer: the shared expert
+    alone, no router.  Route and permute reject it; forward and layer take it with the
+    routed weight pointers NULL and no router weights."""
+    L = fm.lib()
+    dd = fm.desc(2048, 4096, n_experts=0, top_k=0, n_shared=1)
+    need = fm.workspace_bytes(dd, 8)
+    assert need > 0 and fm.workspace_bytes(dd, 32) > need
+    assert fm.workspace_bytes(fm.desc(2048, 4096, n_experts=0, top_k=1), 1) == 0
+    assert fm.workspace_bytes(fm.desc(2048, 4096, n_experts=0, top_k=0, n_shared=0), 1) == 0
+    assert _route(dd, 1, ws=A, nb=need) == fm.ERR_SHAPE
+    assert L.flint_moe_permute(ctypes.byref(dd), 4, A, A, A, A, A, None, 0, None) == fm.ERR_SHAPE
+    dense_w = fm.Weights(fm.WFMT_BF16, None, None, None, A, A, A).c_struct()
+    routed_w = _weights()
+    # routing arguments may be NULL; routed weights must be absent
+    assert _forward(dd, dense_w, 8, nb=need - 1, ids=None, tw=None, off=None, sa=None,
+                    ap=None) == fm.ERR_WORKSPACE
+    assert _forward(dd, routed_w, 8, nb=need) == fm.ERR_FORMAT
+    assert _forward(dd, dense_w, 8, nb=need, y=None) == fm.ERR_NULL
+    assert _forward(dd, fm.Weights(fm.WFMT_BF16, None, None, None).c_struct(), 8, nb=need) == fm.ERR_NULL
+    nv = fm.Weights(fm.WFMT_NVFP4, None, None, None, A, A, A, sh_gate_sf=A, sh_up_sf=A,
+                    sh_down_sf=A, sh_ts=A, gate_ts=A).c_struct()
+    assert _forward(dd, nv, 8, nb=need) == fm.ERR_FORMAT
+    assert L.flint_moe_layer(ctypes.byref(dd), ctypes.byref(dense_w), 8, A, None, None, A, None,
+                             A, 16, None) == fm.ERR_WORKSPACE
+    assert L.flint_moe_layer(ctypes.byref(dd), ctypes.byref(dense_w), 8, A, None, None, None,
+                             None, A, need, None) == fm.ERR_NULL

@@ -183,3 +183,67 @@ def test_single_token_launch_reuses_workspace(fmt):
         assert head[1] == 0, "a wait timed out"
         assert head[0] == n_call + 1, head
         _say("layer %d fmt %d: max rel %.2e rel L1 %.2e" % (layer, fmt, rm, rl))
+
+
+# ---------------------------------------------------------------- NVFP4 prefill
+def test_full_prefill_nvfp4_8192():
+    """T = 8192 on the grouped NVFP4 path.  Weights for the experts of the sampled tokens
+    (host quantisation of all 257 would take minutes); the other experts hold zeros on
+    both sides, and their tiles still run."""
+    H, I, E, k, T = 2048, 768, 256, 6, 8192
+    toks = np.unique(np.concatenate([np.arange(0, T, 523), [T - 1]])).astype(np.int64)
+    x = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), 1.0)
+    Wr = dg.normal_f32((E, H), 0, dg.stream_id(0, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+    ids = oracle.select(oracle.router(x[toks], Wr), k)
+    c = Case(T, H, I, E, k, fmt=fm.WFMT_NVFP4, experts=sorted(set(ids.reshape(-1).tolist())))
+    _parity(c, tokens=toks)
+
+
+# ---------------------------------------------------------------- dense SwiGLU layer
+def _dense_check(T, H, I, fmt, layer=0, tokens=None, three_call=False):
+    """n_experts = 0: y = bf16(down(silu(gate x) * up x)) with the shared-expert pointers,
+    against the reference's SwiGLU expert (sum in fp64) for each checked token."""
+    _say("dense T=%d H=%d I=%d fmt=%d" % (T, H, I, fmt))
+    c = Case(T, H, I, 0, 0, S=1, fmt=fmt, layer=layer).upload()
+    w = c.weights
+    w.gate = w.up = w.down = None
+    w.gate_sf = w.up_sf = w.down_sf = w.gate_ts = w.up_ts = w.down_ts = None
+    y = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    ws = c.workspace()
+    if three_call:
+        fm.forward(c.desc, w, T, c.d_x, None, None, None, None, None, y, ws)
+    else:
+        fm.layer(c.desc, w, T, c.d_x, None, None, y, ws)
+    torch.cuda.synchronize()
+    tok = np.arange(T) if tokens is None else tokens
+    yg = dg.bf16_bits_to_f32(y.cpu().numpy().view(np.uint16)[tok]).astype(np.float64)
+    xf = dg.bf16_bits_to_f32(c.x).astype(np.float64)
+    ref = np.stack([oracle.expert_ffn(c.shared, 0, xf[t]) for t in tok])
+    d = np.abs(yg - ref)
+    assert np.all(np.isfinite(yg))
+    rm, rl = d.max() / np.abs(ref).max(), d.sum() / np.abs(ref).sum()
+    _say("  ok: max rel %.2e, rel L1 %.2e" % (rm, rl))
+    from moe_cases import MAX_REL, MEAN_REL
+    assert rm <= MAX_REL and rl <= MEAN_REL, (rm, rl)
+
+
+@pytest.mark.parametrize("T", [1, 5, 32, 33, 300])
+def test_dense_tiny(T):
+    _dense_check(T, 256, 128, fm.WFMT_BF16)
+
+
+def test_dense_tiny_three_call_and_nvfp4():
+    _dense_check(7, 256, 128, fm.WFMT_BF16, three_call=True)
+    _dense_check(40, 256, 128, fm.WFMT_BF16, three_call=True)
+    for T in (1, 8, 100):
+        _dense_check(T, 256, 256, fm.WFMT_NVFP4)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_dense_full_decode(T):
+    _dense_check(T, 2048, 4096, fm.WFMT_BF16, layer=1)
+
+
+def test_dense_full_prefill_8192():
+    toks = np.unique(np.concatenate([np.arange(0, 8192, 1021), [8191]])).astype(np.int64)
+    _dense_check(8192, 2048, 4096, fm.WFMT_BF16, layer=1, tokens=toks)
