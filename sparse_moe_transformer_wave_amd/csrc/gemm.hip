@@ -2,8 +2,10 @@
 //
 // Prefill is compute-heavy rather than weight-bound (recipes.vllm.ai "RecursiveSI/flint",
 // Benchmarking: the NVFP4 checkpoint barely changes the 8K-token prefill time), so the
-// expert FFNs run on bf16 MFMA with fp32 accumulation, LDS-staged tiles and a register
-// prefetch of the next K step.
+// expert FFNs run on bf16 MFMA with fp32 accumulation and LDS-staged tiles: bf16 weights
+// through a ring of K stages filled HBM -> LDS directly (gemm_bf16_kernel), NVFP4 weights
+// through registers, where they are dequantised, with a prefetch of the next K step
+// (grouped_gemm_kernel).
 //
 // Work items come from the device plan: one item = (touched expert, 256-row tile of its
 // slots), so an expert of up to 256 rows streams its weights once.  Gate/up: A = the expert's tokens gathered from x, B = 32 gate rows and the same
@@ -23,6 +25,7 @@ constexpr int LDP = BK + 8;  // padded LDS row (bf16 elements): 144 bytes
 constexpr int NT = 1024;     // 16 waves: 4 (M) x 4 (N), 64 x 64 per wave
 constexpr int NP = BM * (BK / 8) / NT;  // 16-byte chunks of A (and of B) staged per thread
 constexpr int kXcds = 8;     // workgroup b runs on XCD b % 8
+constexpr int kRingStages = 4;  // bf16 K-stage ring depth (32 KB per stage)
 
 __device__ __forceinline__ u32x4 ld16g(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
@@ -184,6 +187,150 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
     }
 }
 
+// ---------------------------------------------------------------- bf16: LDS ring
+// The same tiles and work items for bf16 weights, with the K loop rebuilt around the
+// CU's LDS: K runs in stages of 32 through a ring of NS stages (32 KB each: 256 A rows and
+// 256 B rows of 64 bytes), filled HBM -> LDS by global_load_lds_dwordx4 (no registers)
+// NS - 1 stages ahead, so three or four stages of loads are in flight per CU while the
+// MFMAs consume the oldest one, and each stage costs one barrier.  Row R keeps its
+// 16-byte chunk c at slot c ^ ((R >> 2) & 3): the 16 lanes of one MFMA fragment read
+// (rows r, chunk g) and one copy instruction writes 16 whole rows, both without bank
+// conflicts (padding the rows instead left conflicts on both sides).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void lds_copy16(const void *g, uint8_t *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+template <int MODE, int NS>
+__global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int E, int k, WSet w,
+                                                       const uint16_t *__restrict__ asrc,
+                                                       const int32_t *__restrict__ sa, Plan p,
+                                                       uint16_t *__restrict__ out)
+{
+    constexpr int kRow = 64, kTile = 256 * kRow, kStage = 2 * kTile;  // bytes
+    extern __shared__ __attribute__((aligned(16))) uint8_t ring[];     // NS * kStage
+    const int N = MODE == 0 ? 2 * I : H;
+    const int n_tiles = N / BN;
+    int item, nb;
+    xcd_map(blockIdx.x, n_tiles, item, nb);
+    if (item >= p.meta[1]) return;
+    const int code = p.items[item];
+    const int u = code >> 16, mtile = code & 0xffff;
+    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    const bool sh = (e == E);
+    const int m0 = mtile * BM;
+    const int valid = min(BM, cnt - m0);
+    const int K = MODE == 0 ? H : I;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int wm = wave >> 2, wn = wave & 3;
+
+    // Copies: wave w fills A rows and B rows 16 w .. 16 w + 15 of every stage; lane l takes
+    // row 16 w + l / 4, slot l % 4, i.e. logical chunk (l % 4) ^ ((row >> 2) & 3).
+    const int crow = 16 * wave + (lane >> 2);
+    const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);
+    const uint16_t *ap_;
+    const uint16_t *bp_;
+    {
+        const int ri = min(crow, valid - 1);
+        if (MODE == 0) {
+            const int tok = sh ? m0 + ri : sa[base + m0 + ri] / k;
+            ap_ = asrc + (size_t)tok * H + 8 * cchunk;
+        } else {
+            ap_ = asrc + (size_t)(base + m0 + ri) * I + 8 * cchunk;
+        }
+        const WMat *mat;
+        int n;
+        if (MODE == 0) {  // each 64-row wave column: 32 gate rows, then the same 32 up rows
+            const int wcol = crow >> 6, within = crow & 63;
+            mat = (within >> 5) ? &w.up : &w.gate;
+            n = nb * (BN / 2) + wcol * 32 + (within & 31);
+        } else {
+            mat = &w.down;
+            n = nb * BN + crow;
+        }
+        const size_t mb = (size_t)H * I;
+        bp_ = reinterpret_cast<const uint16_t *>(sh ? mat->shared : mat->routed) + (sh ? 0 : (size_t)e * mb) +
+              (size_t)n * K + 8 * cchunk;
+    }
+    uint8_t *const cdst = ring + 1024 * wave;  // + stage * kStage (+ kTile for B)
+    auto issue = [&](int kt) {
+        uint8_t *st = cdst + (size_t)(kt % NS) * kStage;
+        lds_copy16(ap_ + 32 * kt, st);
+        lds_copy16(bp_ + 32 * kt, st + kTile);
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment reads: A row wm*64 + 16 ms + r and B row wn*64 + 16 ns + r, logical chunk g.
+    const int fslot = 16 * (g ^ ((r >> 2) & 3));
+    const int aoff = (wm * 64 + r) * kRow + fslot, boff = kTile + (wn * 64 + r) * kRow + fslot;
+    const int nk = K / 32;  // >= 4
+#pragma unroll
+    for (int s = 0; s < NS - 1; s++)
+        if (s < nk) issue(s);
+    for (int kt = 0; kt < nk; kt++) {
+        // Stage kt has landed for this wave once at most min(NS - 2, nk - 1 - kt) later
+        // stages (two copies each) are still in flight; the barrier makes it true for every
+        // wave and frees the slot read in iteration kt - 1, which stage kt + NS - 1 refills.
+        const int later = nk - 1 - kt;
+        if (later >= NS - 2) wait_vmcnt<2 * (NS - 2)>();
+        else if (NS > 4 && later == 2) wait_vmcnt<4>();
+        else if (later == 1) wait_vmcnt<2>();
+        else wait_vmcnt<0>();
+        // the barrier orders LDS accesses for the hardware; the signal fences keep the
+        // compiler from moving fragment reads or ring copies across it
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1);
+        const uint8_t *st = ring + (size_t)(kt % NS) * kStage;
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ms++) af[ms] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + aoff + ms * 16 * kRow));
+#pragma unroll
+        for (int ns = 0; ns < 4; ns++) bfr[ns] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + boff + ns * 16 * kRow));
+#pragma unroll
+        for (int ms = 0; ms < 4; ms++)
+#pragma unroll
+            for (int ns = 0; ns < 4; ns++) acc[ms][ns] = mfma16x16x32(af[ms], bfr[ns], acc[ms][ns]);
+    }
+
+    // Epilogue.  acc[ms][ns][i] = D[row = wm*64 + ms*16 + 4g + i][brow = wn*64 + ns*16 + r].
+#pragma unroll
+    for (int ms = 0; ms < 4; ms++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = wm * 64 + ms * 16 + 4 * g + i;
+            if (row >= valid) continue;
+            const size_t slot = (size_t)(base + m0 + row);
+            if (MODE == 0) {
+#pragma unroll
+                for (int ns = 0; ns < 2; ns++) {
+                    const int col = nb * (BN / 2) + wn * 32 + ns * 16 + r;
+                    out[slot * I + col] = (uint16_t)f2bf(silu(acc[ms][ns][i]) * acc[ms][ns + 2][i]);
+                }
+            } else {
+#pragma unroll
+                for (int ns = 0; ns < 4; ns++) {
+                    const int col = nb * BN + wn * 64 + ns * 16 + r;
+                    out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i]);
+                }
+            }
+        }
+    }
+}
+
 // y[t][n] = bf16(o[T*k + t][n] + sum_j w[t][j] * o[ap[t*k + j]][n]); 8 columns per thread.
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int S,
                                                       const uint16_t *__restrict__ o,
@@ -235,8 +382,9 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
     const unsigned g1 = (unsigned)(item_slots * (2 * s.I / BN));
     const unsigned g2 = (unsigned)(item_slots * (s.H / BN));
     if (w.fmt == 0) {
-        grouped_gemm_kernel<0, 0><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        grouped_gemm_kernel<1, 0><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        constexpr size_t lds = (size_t)kRingStages * 2 * 256 * 64;
+        gemm_bf16_kernel<0, kRingStages><<<g1, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     } else {
         grouped_gemm_kernel<0, 1><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         grouped_gemm_kernel<1, 1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
