@@ -12,7 +12,9 @@ Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant kernel (b
 flops per launch over its measured duration) and the reference's single-core CPU rate on
 a bounded sample.  --config picks another workload: decode_t8, decode_t32, prefill,
 prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32, nvfp4_prefill, and the dense SwiGLU layer
-(no router, I = 4096) at dense_t1, dense_t32, dense_prefill.
+(no router, I = 4096) at dense_t1, dense_t32, dense_prefill; chain_t1 and nvfp4_chain_t1
+run the single token through all 47 layers with one flint_moe_decode_chain call (token of
+layer l + 1 = bf16(x_l + y_l), formed in the kernel of layer l).
 """
 from __future__ import annotations
 
@@ -39,6 +41,10 @@ CONFIGS = {
     "nvfp4_t8": dict(T=8, fmt=1, layers=47, zipf=False),
     "nvfp4_t32": dict(T=32, fmt=1, layers=47, zipf=False),
     "nvfp4_prefill": dict(T=8192, fmt=1, layers=1, zipf=False),
+    # one token through the 47 layers in one flint_moe_decode_chain call, each layer's token =
+    # bf16(previous token + previous layer's output) formed by the previous layer's kernel
+    "chain_t1": dict(T=1, fmt=0, layers=47, zipf=False, chain=True),
+    "nvfp4_chain_t1": dict(T=1, fmt=1, layers=47, zipf=False, chain=True),
     # dense SwiGLU layers (E = 0, k = 0, the shared expert alone; 16 distinct layers cycled)
     "dense_t1": dict(T=1, fmt=0, layers=16, zipf=False, dense=True),
     "dense_t32": dict(T=32, fmt=0, layers=16, zipf=False, dense=True),
@@ -291,6 +297,11 @@ def main():
         for d in layers:
             fm.layer(desc, d["weights"], T, x, None, None, y, ws)
             touched.append(0)
+    chain = bool(cfg.get("chain"))
+    if chain:  # a single token touches exactly k routed experts in every layer
+        touched = [TOPK] * L
+        ychain = torch.empty((L, H), dtype=torch.int16, device="cuda")
+        refs = fm.layer_refs([(d["weights"], d["Wr"], d["bias"]) for d in layers])
     alg_bytes = [(u + S) * xb + E * H * 4 + 4 * T * H for u in touched]
     flops_layer = 2.0 * T * (TOPK + S) * 3 * H * I
 
@@ -302,17 +313,23 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             st = torch.cuda.current_stream().cuda_stream
-            calls = [fm.layer_ptr_args(desc, d["weights"], T, x, d["Wr"], d["bias"], y,
-                                       ws.data_ptr(), ws.numel(), st) for d in layers]
+            if chain:
+                fn, name = L_lib.flint_moe_decode_chain, "flint_moe_decode_chain"
+                calls = [((ctypes.byref(desc), refs, L, fm.CHAIN_RESIDUAL, x.data_ptr(), ychain.data_ptr(),
+                           None, None, None, ws.data_ptr(), ws.numel(), st), refs)]
+            else:
+                fn, name = L_lib.flint_moe_layer, "flint_moe_layer"
+                calls = [fm.layer_ptr_args(desc, d["weights"], T, x, d["Wr"], d["bias"], y,
+                                           ws.data_ptr(), ws.numel(), st) for d in layers]
             for _ in range(n_steps):
                 for a, _keep in calls:
                     if with_events:
                         e = torch.cuda.Event(enable_timing=True, external=True)
                         e.record()
                         ev.append(e)
-                    rc = L_lib.flint_moe_layer(*a)
+                    rc = fn(*a)
                     if rc:
-                        raise fm.FlintError(rc, "flint_moe_layer")
+                        raise fm.FlintError(rc, name)
             if with_events:
                 e = torch.cuda.Event(enable_timing=True, external=True)
                 e.record()
@@ -339,6 +356,8 @@ def main():
     elapsed_ms = start.elapsed_time(end)
     if evs:
         per_call = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
+        if chain:  # one event interval per chain call of L layers
+            per_call = [t / L for t in per_call for _ in range(L)]
     else:
         per_call = [elapsed_ms / (L * args.steps)] * (L * args.steps)
     log("timed %d steps: %.3f ms" % (args.steps, elapsed_ms))
@@ -353,6 +372,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
                 "kernel": ("flint_moe_layer (dense: plan, gate/up, down, combine kernels)" if E == 0 else
+                           "decode1_kernel (one persistent launch per layer; chain call time / layers)"
+                           if chain else
                            "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
                            "flint_moe_layer (router with selection, gate/up, down, combine kernels)"),
                 "avg_launch_us": round(avg_call_ms * 1e3, 2),
@@ -373,7 +394,9 @@ def main():
         "config": {"workload": ("%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, "
                                 "SwiGLU, %s, %d distinct layers cycled%s"
                                 % (args.config, T, H, I, E, TOPK, S, "bf16" if fmt == 0 else "NVFP4",
-                                   L, ", Zipf(1.1) logit bias" if cfg["zipf"] else "")) if E else
+                                   L, ", Zipf(1.1) logit bias" if cfg["zipf"] else
+                                   ", chained: one flint_moe_decode_chain call per step, token of layer l + 1 = "
+                                   "bf16(x_l + y_l)" if chain else "")) if E else
                                ("%s: T=%d tokens, dense SwiGLU FFN layer (no router), H=%d, I=%d, "
                                 "%s, %d distinct layers cycled" % (args.config, T, H, I,
                                                                    "bf16" if fmt == 0 else "NVFP4", L)),

@@ -34,7 +34,7 @@
  *     their scales must be NULL); flint_moe_route and flint_moe_permute return
  *     FLINT_ERR_SHAPE.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
- *   - A workspace's first 80 KiB hold the single-token path's launch counter, error flag
+ *   - A workspace's first 96 KiB hold the single-token path's launch counter, error flag
  *     and exchange words: zero them once before first use (flint_moe_workspace_init, or
  *     any zero fill) and leave them to the library afterwards.
  */
@@ -121,7 +121,7 @@ typedef struct {
    given weight format.  Returns 0 for an invalid descriptor or T_max < 0. */
 size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int32_t format);
 
-/* Zero the first 80 KiB of a workspace (a small fill kernel on `stream`; no
+/* Zero the first 96 KiB of a workspace (a small fill kernel on `stream`; no
    allocation).  Call once per workspace before its first use. */
 int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
@@ -181,6 +181,41 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
                     const uint16_t *x, const float *w_router, const float *logit_bias,
                     uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* ---- persistent decode across layers ---------------------------------------------- */
+/* One MoE layer of a chain: its expert weights, router weights [E][H] fp32 and optional
+   logit bias [E] (device pointers, checked like flint_moe_layer's). */
+typedef struct {
+    flint_moe_weights weights;
+    const float *w_router;
+    const float *logit_bias;
+} flint_moe_layer_ref;
+
+enum {
+    FLINT_CHAIN_RESIDUAL = 1  /* the next layer's token is bf16(x_l + y_l) instead of y_l */
+};
+
+/* A single token through n_layers MoE layers, one after the other, in few launches:
+     x_0 = x;  y_l = layer_l(x_l) exactly as flint_moe_layer computes it for T = 1;
+     x_{l+1} = y_l, or bf16(x_l + y_l) (one fp32 sum, rounded once) with FLINT_CHAIN_RESIDUAL.
+   The pages' GB200 runtime has a low-latency decode path for up to 8 requests and the
+   Apple runtime a Metal megakernel (recipes.vllm.ai "RecursiveSI/flint", Overview;
+   mrchatgpt.org explainer, section 4, the item on kernels).  Here every layer is the
+   single-token persistent launch of flint_moe_layer; its last phase also forms the next
+   layer's token and leaves it in the workspace head for the next launch, so the chain
+   costs no work between layers.  (Running several layers inside one launch, trading the
+   token through tagged words, was measured slower on this GPU: the layer loop costs the
+   kernel registers that its single-layer form keeps for loads in flight.)
+   layers: host array [n_layers] (read during the call only).  All layers share `desc` and
+   one weight format.  x: bf16 [H]; y: bf16 [n_layers][H], every layer's output y_l;
+   topk_ids / topk_w: [n_layers][k] or NULL; logits: [n_layers][E] fp32 or NULL.  Needs the single-token persistent path:
+   E >= 1, hidden <= 2048, inter <= 1024, k <= 8, and a device with at least 256 CUs
+   (FLINT_ERR_SHAPE otherwise).  ws: at least flint_moe_workspace_bytes(desc, 1, format)
+   bytes, initialised once (flint_moe_workspace_init).  0 <= n_layers <= 4096. */
+int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref *layers,
+                           int32_t n_layers, uint32_t flags, const uint16_t *x, uint16_t *y,
+                           int32_t *topk_ids, float *topk_w, float *logits, void *ws,
+                           size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

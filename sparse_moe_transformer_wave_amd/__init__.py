@@ -24,9 +24,11 @@ LIB_PATH = os.path.join(_HERE, "libflint_moe.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_FORMAT, ERR_HIP = range(7)
 WFMT_BF16, WFMT_NVFP4 = 0, 1
 ROUTE_LOGITS_IN = 1
+CHAIN_RESIDUAL = 1
 
 EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_workspace_init", "flint_moe_status_string",
-            "flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer")
+            "flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer",
+            "flint_moe_decode_chain")
 
 
 class FlintError(RuntimeError):
@@ -47,6 +49,10 @@ class _Weights(ctypes.Structure):
             "gate", "up", "down", "sh_gate", "sh_up", "sh_down",
             "gate_sf", "up_sf", "down_sf", "sh_gate_sf", "sh_up_sf", "sh_down_sf",
             "gate_ts", "up_ts", "down_ts", "sh_ts")]
+
+
+class _LayerRef(ctypes.Structure):
+    _fields_ = [("weights", _Weights), ("w_router", ctypes.c_void_p), ("logit_bias", ctypes.c_void_p)]
 
 
 class _Routing(ctypes.Structure):
@@ -76,7 +82,10 @@ def lib():
         L.flint_moe_permute.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.flint_moe_forward.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.flint_moe_layer.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
-        for f in ("flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer"):
+        L.flint_moe_decode_chain.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_uint32, vp, vp, vp, vp,
+                                             vp, vp, sz, vp]
+        for f in ("flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer",
+                  "flint_moe_decode_chain"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -198,6 +207,28 @@ def layer(d: Desc, weights: Weights, T: int, x, w_router, bias, y, ws, routing: 
                                _ptr(bias), _ptr(y), None if r is None else ctypes.byref(r),
                                _ptr(ws), _nbytes(ws), _stream(stream))
     _check(rc, "flint_moe_layer")
+
+
+def layer_refs(layers):
+    """ctypes array of flint_moe_layer_ref from (Weights, w_router, logit_bias) triples."""
+    arr = (_LayerRef * max(len(layers), 1))()
+    for i, (w, wr, bias) in enumerate(layers):
+        arr[i].weights = w.c_struct()
+        arr[i].w_router = _ptr(wr)
+        arr[i].logit_bias = _ptr(bias)
+    return arr
+
+
+def decode_chain(d: Desc, layers, x, y, ws, topk_ids=None, topk_w=None, logits=None,
+                 residual=False, stream=None):
+    """One token through len(layers) layers (flint_moe_decode_chain); layers = list of
+    (Weights, w_router, logit_bias); y: [L][H] bf16 (int16 tensor)."""
+    refs = layer_refs(layers)
+    rc = lib().flint_moe_decode_chain(ctypes.byref(d), refs, len(layers),
+                                      CHAIN_RESIDUAL if residual else 0, _ptr(x), _ptr(y),
+                                      _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(ws), _nbytes(ws),
+                                      _stream(stream))
+    _check(rc, "flint_moe_decode_chain")
 
 
 def layer_ptr_args(d: Desc, weights: Weights, T: int, x, w_router, bias, y, ws_ptr: int,

@@ -12,6 +12,7 @@ using namespace flint;
 namespace {
 
 constexpr int64_t kMaxT = 65536;
+constexpr int32_t kMaxChainLayers = 4096;
 thread_local char g_msg[256];
 thread_local hipError_t g_last_hip = hipSuccess;
 
@@ -350,6 +351,51 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
         if (rc) return rc;
     }
     return forward_impl(s, wset_of(weights), T, x, tw, sa, ap, y, ws, L, plan, st);
+}
+
+int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref *layers,
+                           int32_t n_layers, uint32_t flags, const uint16_t *x, uint16_t *y,
+                           int32_t *topk_ids, float *topk_w, float *logits, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (desc->n_experts == 0 || n_layers < 0 || n_layers > kMaxChainLayers) return FLINT_ERR_SHAPE;
+    if (flags & ~(uint32_t)FLINT_CHAIN_RESIDUAL) return FLINT_ERR_FORMAT;
+    if (n_layers == 0) return FLINT_OK;
+    if (!layers || !x || !y || !ws) return FLINT_ERR_NULL;
+    const void *ptrs[] = {x, y, topk_ids, topk_w, logits, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FLINT_ERR_ALIGN;
+    const int fmt = layers[0].weights.format;
+    for (int l = 0; l < n_layers; l++) {
+        rc = check_weights(desc, &layers[l].weights);
+        if (rc) return rc;
+        if (layers[l].weights.format != fmt) return FLINT_ERR_FORMAT;
+        if (!layers[l].w_router) return FLINT_ERR_NULL;
+        if (!aligned16(layers[l].w_router) || !aligned16(layers[l].logit_bias)) return FLINT_ERR_ALIGN;
+    }
+    const Shape s = shape_of(desc);
+    if (ws_bytes < ws_layout(s, 1).total) return FLINT_ERR_WORKSPACE;
+    if (!decode1_supported(s, fmt)) return FLINT_ERR_SHAPE;
+    hipStream_t st = (hipStream_t)stream;
+    for (int l0 = 0; l0 < n_layers; l0 += kChainChunk) {
+        const int n = n_layers - l0 < kChainChunk ? n_layers - l0 : kChainChunk;
+        WSet w[kChainChunk];
+        const float *wr[kChainChunk], *bias[kChainChunk];
+        for (int i = 0; i < n; i++) {
+            w[i] = wset_of(&layers[l0 + i].weights);
+            wr[i] = layers[l0 + i].w_router;
+            bias[i] = layers[l0 + i].logit_bias;
+        }
+        rc = hip_status(launch_decode_chain(
+            s, w, wr, bias, n, flags & FLINT_CHAIN_RESIDUAL, l0 == 0 ? x : nullptr, l0 + n < n_layers,
+            y + (size_t)l0 * s.H, topk_ids ? topk_ids + (size_t)l0 * s.k : nullptr,
+            topk_w ? topk_w + (size_t)l0 * s.k : nullptr, logits ? logits + (size_t)l0 * s.E : nullptr,
+            ws, st));
+        if (rc) return rc;
+    }
+    return FLINT_OK;
 }
 
 }  // extern "C"

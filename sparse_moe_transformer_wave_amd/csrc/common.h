@@ -81,12 +81,21 @@ hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, co
 // Single-token layer in one persistent launch (decode1.hip).  `head` = the workspace's
 // first kSyncBytes (launch counter and exchange words; zero before first use).
 // decode1_supported also checks that the current device has a CU for every workgroup.
-constexpr size_t kSyncBytes = 80 * 1024;
+constexpr size_t kSyncBytes = 96 * 1024;
 bool decode1_supported(const Shape &s, int fmt);
 hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, const float *Wr,
                           const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
                           int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
                           hipStream_t st);
+// One token through L layers, one single-token launch per layer: layer l + 1's token is
+// y_l, or bf16(x_l + y_l) with `residual`, handed on through the workspace head.  x = null
+// starts from the token a previous call left there (`hand_on`).  y: [L][H]; ids, tw: [L][k],
+// logits [L][E], or null.
+constexpr int kChainChunk = 16;  // layers whose descriptors the host gathers at a time
+hipError_t launch_decode_chain(const Shape &s, const WSet *w, const float *const *Wr,
+                               const float *const *bias, int L, bool residual, const uint16_t *x,
+                               bool hand_on, uint16_t *y, int32_t *ids, float *tw, float *logits,
+                               void *head, hipStream_t st);
 
 // Streaming path (T <= kGemvMaxT) from an existing plan.
 hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,

@@ -45,9 +45,12 @@ constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
 // Workspace words of this launch (the zero-initialised head of the workspace):
 // u32 [0] launch counter, u32 [1] error flag; u64 exchange words for the logits at byte
 // 1024 (one per workgroup) and for h at byte 3072 ([k + 1][I], slot k = shared expert).
+// A chain of layers hands each token to the next launch through the bf16 [2048] buffer at
+// kXNextOff.
 constexpr int kCtlEpoch = 0, kCtlError = 1;
 constexpr size_t kXLogOff = 1024, kXHOff = kXLogOff + 8 * kG;
-static_assert(kXHOff + 8 * (size_t)(kMaxK + 1) * 1024 <= kSyncBytes, "exchange words exceed the head");
+constexpr size_t kXNextOff = kXHOff + 8 * (size_t)(kMaxK + 1) * 1024;
+static_assert(kXNextOff + 2 * 2048 <= kSyncBytes, "exchange words exceed the head");
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -149,10 +152,12 @@ struct D1Args {
     const uint16_t *x;
     const float *Wr, *bias;
     uint16_t *y;
+    uint16_t *xnext;  // null, or receives the next layer's token: y, or bf16(x + y) with `residual`
+    int residual;
     float *logits;
     int32_t *ids;
     float *tw;
-    int32_t *counts, *offsets, *sa, *ap;
+    int32_t *counts, *offsets, *sa, *ap;  // null in a chain
     uint32_t *ctl;   // launch counter, error flag
     uint64_t *xlog;  // [256] exchange words: logit of expert b (workgroup b)
     uint64_t *xh;    // [k + S][I] exchange words: slot j < k = j-th selected expert, slot k = shared
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
             }
             const float l = wave_sum(acc) + (a.bias ? a.bias[e] : 0.f);
             if (lane == 0) {
-                a.logits[e] = l;
+                if (a.logits) a.logits[e] = l;
                 put_word(a.xlog + b, tag, l);
             }
         } else if (lane == 0) {
@@ -413,22 +418,26 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         put_word(a.xh + (size_t)j * I + i0 + p, tag, silu(sh.g[j][p]) * sh.u[j][p]);
     }
     if (b == 0 && tid < 64) {  // publish the routing tensors (the single token: t = 0)
-        for (int e = tid; e <= E; e += 64) {
-            int below = 0, eq = 0;
-            for (int j = 0; j < k; j++) {
-                below += sh.ids[j] < e;
-                eq += sh.ids[j] == e;
-            }
-            a.offsets[e] = below;
-            if (e < E) a.counts[e] = eq;
-        }
         if (tid < k) {
-            int pos = 0;
-            for (int j = 0; j < k; j++) pos += sh.ids[j] < sh.ids[tid];
-            a.ids[tid] = sh.ids[tid];
-            a.tw[tid] = sh.wt[tid];
-            a.sa[pos] = tid;
-            a.ap[tid] = pos;
+            if (a.ids) a.ids[tid] = sh.ids[tid];
+            if (a.tw) a.tw[tid] = sh.wt[tid];
+        }
+        if (a.counts) {
+            for (int e = tid; e <= E; e += 64) {
+                int below = 0, eq = 0;
+                for (int j = 0; j < k; j++) {
+                    below += sh.ids[j] < e;
+                    eq += sh.ids[j] == e;
+                }
+                a.offsets[e] = below;
+                if (e < E) a.counts[e] = eq;
+            }
+            if (tid < k) {
+                int pos = 0;
+                for (int j = 0; j < k; j++) pos += sh.ids[j] < sh.ids[tid];
+                a.sa[pos] = tid;
+                a.ap[tid] = pos;
+            }
         }
     }
 
@@ -483,7 +492,12 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     for (int n = tid; n < rows_h; n += 512) {
         float acc = S ? sh.o[k][n] : 0.f;
         for (int j = 0; j < k; j++) acc += sh.wt[j] * sh.o[j][n];
-        a.y[n0 + n] = (uint16_t)f2bf(acc);
+        const uint32_t yv = f2bf(acc);
+        a.y[n0 + n] = (uint16_t)yv;
+        // The next layer's token (a chain): this launch read all of x in phase 1, before any
+        // workgroup got here, so x and xnext may be the same buffer.
+        if (a.xnext)
+            a.xnext[n0 + n] = (uint16_t)(a.residual ? f2bf(bf2f(a.x[n0 + n]) + bf2f(yv)) : yv);
     }
 }
 
@@ -520,20 +534,45 @@ bool decode1_supported(const Shape &s, int fmt)
            d1_dyn_bytes(s, fmt) + sizeof(D1Shared) <= 160 * 1024 && device_cus() >= kG;
 }
 
+static hipError_t launch_d1(const Shape &s, int fmt, const D1Args &a, hipStream_t st)
+{
+    const size_t dyn = d1_dyn_bytes(s, fmt);
+    // HIP on gfx950 takes up to the CU's 160 KB of LDS per workgroup without an opt-in.
+    if (fmt == 0) decode1_kernel<0><<<kG, 512, dyn, st>>>(a);
+    else decode1_kernel<1><<<kG, 512, dyn, st>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, const float *Wr,
                           const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
                           int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
                           hipStream_t st)
 {
     char *hb = static_cast<char *>(head);
-    D1Args a{s.H, s.I, s.E, s.k, s.S, s.renorm, w, x, Wr, bias, y, logits, ids, tw, counts, offsets,
-             sa, ap, reinterpret_cast<uint32_t *>(hb), reinterpret_cast<uint64_t *>(hb + kXLogOff),
-             reinterpret_cast<uint64_t *>(hb + kXHOff)};
-    const size_t dyn = d1_dyn_bytes(s, w.fmt);
-    // HIP on gfx950 takes up to the CU's 160 KB of LDS per workgroup without an opt-in.
-    if (w.fmt == 0) decode1_kernel<0><<<kG, 512, dyn, st>>>(a);
-    else decode1_kernel<1><<<kG, 512, dyn, st>>>(a);
-    return hipGetLastError();
+    D1Args a{s.H, s.I, s.E, s.k, s.S, s.renorm, w, x, Wr, bias, y, nullptr, 0, logits, ids, tw,
+             counts, offsets, sa, ap, reinterpret_cast<uint32_t *>(hb),
+             reinterpret_cast<uint64_t *>(hb + kXLogOff), reinterpret_cast<uint64_t *>(hb + kXHOff)};
+    return launch_d1(s, w.fmt, a, st);
+}
+
+hipError_t launch_decode_chain(const Shape &s, const WSet *w, const float *const *Wr,
+                               const float *const *bias, int L, bool residual, const uint16_t *x,
+                               bool hand_on, uint16_t *y, int32_t *ids, float *tw, float *logits,
+                               void *head, hipStream_t st)
+{
+    char *hb = static_cast<char *>(head);
+    uint16_t *xnext = reinterpret_cast<uint16_t *>(hb + kXNextOff);
+    for (int l = 0; l < L; l++) {
+        D1Args a{s.H, s.I, s.E, s.k, s.S, s.renorm, w[l], l == 0 && x ? x : xnext, Wr[l], bias[l],
+                 y + (size_t)l * s.H, l + 1 < L || hand_on ? xnext : nullptr, residual ? 1 : 0,
+                 logits ? logits + (size_t)l * s.E : nullptr, ids ? ids + (size_t)l * s.k : nullptr,
+                 tw ? tw + (size_t)l * s.k : nullptr, nullptr, nullptr, nullptr, nullptr,
+                 reinterpret_cast<uint32_t *>(hb), reinterpret_cast<uint64_t *>(hb + kXLogOff),
+                 reinterpret_cast<uint64_t *>(hb + kXHOff)};
+        const hipError_t e = launch_d1(s, w[l].fmt, a, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace flint

@@ -191,6 +191,8 @@ def check_routing(c: Case, g, report=None):
         np.testing.assert_array_equal(np.sort(g["topk_ids"][clear], 1), np.sort(own[clear], 1))
         if report is not None:
             report["near_ties"] = int((~clear).sum())
+    if "counts" not in g:  # a call that returns no grouping tensors
+        return w64
     counts, offsets, sa, ap = oracle.permute(g["topk_ids"], c.E)
     np.testing.assert_array_equal(g["counts"], counts)
     np.testing.assert_array_equal(g["offsets"], offsets)

@@ -138,3 +138,32 @@ def test_dense_layer_validation():
                              A, 16, None) == fm.ERR_WORKSPACE
     assert L.flint_moe_layer(ctypes.byref(dd), ctypes.byref(dense_w), 8, A, None, None, None,
                              None, A, need, None) == fm.ERR_NULL
+
+
+def test_decode_chain_validation():
+    """flint_moe_decode_chain checks every layer's weights before any HIP call."""
+    L = fm.lib()
+    d = fm.desc(2048, 768)
+    need = fm.workspace_bytes(d, 1)
+
+    def chain(layers, n=None, flags=0, x=A, y=A, ids=None, tw=None, ws=A, nb=need, dd=d):
+        refs = fm.layer_refs(layers)
+        return L.flint_moe_decode_chain(ctypes.byref(dd), refs if layers else None,
+                                        len(layers) if n is None else n, flags, x, y, ids, tw,
+                                        None, ws, nb, None)
+
+    good = (fm.Weights(fm.WFMT_BF16, A, A, A, A, A, A), A, None)
+    assert chain([], n=0) == fm.OK
+    assert chain([good], n=-1) == fm.ERR_SHAPE
+    assert chain([good], n=5000) == fm.ERR_SHAPE
+    assert chain([good], dd=fm.desc(2048, 768, n_experts=0, top_k=0)) == fm.ERR_SHAPE
+    assert chain([good], flags=2) == fm.ERR_FORMAT
+    assert chain([], n=1) == fm.ERR_NULL
+    assert chain([good], x=None) == fm.ERR_NULL
+    assert chain([good], y=MIS) == fm.ERR_ALIGN
+    assert chain([good, (fm.Weights(fm.WFMT_BF16, A, A, None, A, A, A), A, None)]) == fm.ERR_NULL
+    assert chain([good, (good[0], None, None)]) == fm.ERR_NULL
+    assert chain([good, (good[0], A, MIS)]) == fm.ERR_ALIGN
+    nv = fm.Weights(fm.WFMT_NVFP4, A, A, A, A, A, A, A, A, A, A, A, A, A, A, A, A)
+    assert chain([good, (nv, A, None)]) == fm.ERR_FORMAT  # formats differ
+    assert chain([good], nb=need - 1) == fm.ERR_WORKSPACE

@@ -247,3 +247,93 @@ def test_dense_full_decode(T):
 def test_dense_full_prefill_8192():
     toks = np.unique(np.concatenate([np.arange(0, 8192, 1021), [8191]])).astype(np.int64)
     _dense_check(8192, 2048, 4096, fm.WFMT_BF16, layer=1, tokens=toks)
+
+
+# ---------------------------------------------------------------- persistent decode chain
+def _next_token(x_bits, y_bits, residual):
+    """x_{l+1}: y_l, or bf16(x_l + y_l) from one fp32 sum (round to nearest even)."""
+    if not residual:
+        return y_bits.copy()
+    s = (dg.bf16_bits_to_f32(x_bits).astype(np.float32) + dg.bf16_bits_to_f32(y_bits).astype(np.float32))
+    return dg.f32_to_bf16_bits(s.astype(np.float32))
+
+
+def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
+    """flint_moe_decode_chain over L layers, each layer checked against the reference on
+    the token the GPU fed it (recomputed on the host from the GPU's y of the previous
+    layer), with the two-stage protocol of a single-token layer."""
+    _say("chain H=%d I=%d E=%d k=%d fmt=%d L=%d residual=%d" % (H, I, E, k, fmt, L, residual))
+    x0 = dg.normal_bf16((1, H), 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
+    cases = []
+    xh = x0
+    for l in range(L):
+        experts = None
+        if predict_experts:  # the reference's own chain decides which experts get weights
+            Wr = dg.normal_f32((E, H), 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+            experts = sorted(set(oracle.select(oracle.router(xh, Wr), k).reshape(-1).tolist()))
+        c = Case(1, H, I, E, k, fmt=fmt, layer=l, experts=experts, x=xh).upload()
+        cases.append(c)
+        if predict_experts and l + 1 < L:
+            lg = oracle.router(xh, c.Wr)
+            ids = oracle.select(lg, k)
+            yr = oracle.moe_tokens(c.routed, c.shared, xh, ids, oracle.weights(lg, ids, True))
+            xh = _next_token(xh, dg.f32_to_bf16_bits(yr.astype(np.float32)), residual)
+    d = cases[0].desc
+    y = torch.zeros((L, H), dtype=torch.int16, device="cuda")
+    ids = torch.zeros((L, k), dtype=torch.int32, device="cuda")
+    tw = torch.zeros((L, k), dtype=torch.float32, device="cuda")
+    lg = torch.zeros((L, E), dtype=torch.float32, device="cuda")
+    ws = fm.workspace(d, 1, fmt) if ws is None else ws
+    fm.decode_chain(d, [(c.weights, c.d_Wr, None) for c in cases], cases[0].d_x, y, ws, ids, tw, lg,
+                    residual=residual)
+    torch.cuda.synchronize()
+    yg, idg, twg, lgg = (t.cpu().numpy() for t in (y, ids, tw, lg))
+    yg = yg.view(np.uint16)
+    xl = x0
+    for l, c in enumerate(cases):
+        c.x = xl  # the token the GPU fed layer l
+        g = {"logits": lgg[l:l + 1], "topk_ids": idg[l:l + 1], "topk_w": twg[l:l + 1], "y": yg[l:l + 1]}
+        w64 = check_routing(c, g)
+        rm, rl = check_forward(c, g, w64)
+        _say("  layer %d: max rel %.2e, rel L1 %.2e" % (l, rm, rl))
+        xl = _next_token(xl, yg[l:l + 1], residual)
+    head = ws[:8].view(torch.int32).cpu().numpy()
+    assert head[1] == 0, "a wait timed out"
+    return ws, head
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_chain_tiny(residual):
+    # Without the residual the token shrinks about quadratically per layer (x -> ~1e-2 ->
+    # ~1e-6 -> ~1e-14 -> ~1e-30 here), and the fifth layer's h underflows fp32 while the fp64
+    # reference keeps ~1e-62: four layers are the meaningful length of that chain.
+    _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 7 if residual else 4, residual)
+
+
+def test_chain_tiny_two_launches_and_counter():
+    """20 layers (the host gathers layer descriptors 16 at a time, so the token crosses
+    that boundary too); the launch counter advances once per layer, and a following
+    single-token layer call on the same workspace is still correct."""
+    ws, head = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 20, True)
+    assert head[0] == 20, head
+    c = Case(1, 256, 128, 256, 6, layer=3).upload()
+    out = c.alloc_out()
+    routing = {kk: out[kk] for kk in ("logits", "topk_ids", "topk_w", "counts", "offsets",
+                                      "sorted_assign", "assign_pos")}
+    fm.layer(c.desc, c.weights, 1, c.d_x, c.d_Wr, None, out["y"], ws, routing)
+    torch.cuda.synchronize()
+    from moe_cases import to_host
+    g = to_host(out, c)
+    check_forward(c, g, check_routing(c, g))
+    head = ws[:8].view(torch.int32).cpu().numpy()
+    assert head[0] == 21 and head[1] == 0, head
+
+
+def test_chain_tiny_nvfp4():
+    # I = 256: a workgroup's NVFP4 down rows (codes + scales) must fill whole 16-byte chunks
+    _chain_check(256, 256, 256, 6, fm.WFMT_NVFP4, 3, True)
+
+
+@pytest.mark.parametrize("fmt", [fm.WFMT_BF16, fm.WFMT_NVFP4])
+def test_chain_full(fmt):
+    _chain_check(2048, 768, 256, 6, fmt, 3, True, predict_experts=True)
