@@ -20,6 +20,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 
 FMT_BF16 = 0
 FMT_NVFP4 = 1
+FMT_INT4 = 2
 
 
 def build(force: bool = False) -> str:
@@ -73,6 +74,12 @@ def lib():
         L.oracle_moe_tokens.restype = None
         L.oracle_nvfp4_quantize.argtypes = [i64, i64, vp, vp, vp, ctypes.POINTER(ctypes.c_float)]
         L.oracle_nvfp4_quantize.restype = None
+        L.oracle_int4_value.restype = ctypes.c_double
+        L.oracle_int4_value.argtypes = [ctypes.c_uint32]
+        L.oracle_int4_quantize.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_int4_quantize.restype = None
+        L.oracle_matrix_at.restype = ctypes.c_double
+        L.oracle_matrix_at.argtypes = [ctypes.POINTER(_Matrix), i64, i64, i64]
         _lib = L
     return _lib
 
@@ -109,6 +116,28 @@ def nvfp4_quantize(W: np.ndarray):
     st = ctypes.c_float(0.0)
     lib().oracle_nvfp4_quantize(N, K, _p(W), _p(q), _p(sb), ctypes.byref(st))
     return q, sb, float(st.value)
+
+
+def int4_value(code: int) -> float:
+    return lib().oracle_int4_value(code)
+
+
+def int4_quantize(W: np.ndarray):
+    """W [N][K] (float64) -> (q uint8 [N][K/2], s bf16 bits uint16 [N][K/128])."""
+    W = np.ascontiguousarray(W, dtype=np.float64)
+    N, K = W.shape
+    assert K % 128 == 0
+    q = np.empty((N, K // 2), np.uint8)
+    sc = np.empty((N, K // 128), np.uint16)
+    lib().oracle_int4_quantize(N, K, _p(W), _p(q), _p(sc))
+    return q, sc
+
+
+def matrix_at(fmt: int, data: np.ndarray, scale, K: int, n: int, k: int, tensor_scale=1.0) -> float:
+    """Element (n, k) of one matrix as the reference reads it."""
+    m = _Matrix(fmt, data.ctypes.data, None if scale is None else scale.ctypes.data,
+                float(tensor_scale))
+    return lib().oracle_matrix_at(ctypes.byref(m), K, n, k)
 
 
 # ------------------------------------------------------------------------ layer steps
@@ -165,6 +194,8 @@ class Experts:
     bf16:  gate [n][I][H], up [n][I][H], down [n][H][I] as uint16 bits.
     nvfp4: dict of q/sb/st triples per matrix:  q_gate [n][I][H/2], sb_gate [n][I][H/16],
            st_gate [n] float32, and likewise for up and down ([n][H][I/2], [n][H][I/16]).
+    int4:  q/sb pairs per matrix: q_gate [n][I][H/2] packed nibbles, sb_gate [n][I][H/128]
+           bf16 scale bits (uint16), likewise for up and down.
     """
 
     def __init__(self, fmt: int, H: int, I: int, arrays: dict):
@@ -181,6 +212,11 @@ class Experts:
             a = self.arrays[name]
             assert a.dtype == np.uint16 and a.shape[1:] == (N, K)
             return _Matrix(FMT_BF16, a[e].ctypes.data, None, 0.0)
+        if self.fmt == FMT_INT4:
+            q, sb = self.arrays["q_" + name], self.arrays["sb_" + name]
+            assert q.dtype == np.uint8 and q.shape[1:] == (N, K // 2) and sb.dtype == np.uint16
+            assert sb.shape[1:] == (N, K // 128)
+            return _Matrix(FMT_INT4, q[e].ctypes.data, sb[e].ctypes.data, 1.0)
         q, sb, st = self.arrays["q_" + name], self.arrays["sb_" + name], self.arrays["st_" + name]
         assert q.dtype == np.uint8 and q.shape[1:] == (N, K // 2) and sb.shape[1:] == (N, K // 16)
         return _Matrix(FMT_NVFP4, q[e].ctypes.data, sb[e].ctypes.data, float(st[e]))

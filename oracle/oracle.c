@@ -47,11 +47,24 @@ double oracle_e4m3_value(uint32_t code)
     return (code & 0x80u) ? -mag : mag;
 }
 
+/* A nibble read as a two's complement 4-bit integer: bit 3 has weight -8. */
+double oracle_int4_value(uint32_t code)
+{
+    return (double)(int)(code & 7u) - ((code & 8u) ? 8.0 : 0.0);
+}
+
 double oracle_matrix_at(const oracle_matrix *m, int64_t K, int64_t n, int64_t k)
 {
     if (m->format == ORACLE_FMT_BF16) {
         const uint16_t *w = (const uint16_t *)m->data;
         return bf16_bits_to_double(w[n * K + k]);
+    }
+    if (m->format == ORACLE_FMT_INT4) {
+        const uint8_t *q = (const uint8_t *)m->data;
+        uint8_t byte = q[n * (K / 2) + k / 2];
+        uint32_t code = (k % 2 == 0) ? (byte & 15u) : (byte >> 4);
+        const uint16_t *sc = (const uint16_t *)m->block_scale;
+        return oracle_int4_value(code) * bf16_bits_to_double(sc[n * (K / 128) + k / 128]);
     }
     const uint8_t *q = (const uint8_t *)m->data;
     uint8_t byte = q[n * (K / 2) + k / 2];
@@ -270,6 +283,47 @@ void oracle_nvfp4_quantize(int64_t N, int64_t K, const double *W, uint8_t *q, ui
                 uint32_t c0 = (bs == 0.0) ? 0u : oracle_e2m1_encode(blk[i] / bs);
                 uint32_t c1 = (bs == 0.0) ? 0u : oracle_e2m1_encode(blk[i + 1] / bs);
                 q[n * (K / 2) + (b * 16 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+}
+
+/* double -> bf16 bits, round to nearest even (finite values in the normal bf16 range, or
+   zero): 8 significant bits. */
+static uint16_t double_to_bf16_rne(double v)
+{
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+    int e2;
+    double f = frexp(fabs(v), &e2);      /* |v| = f * 2^e2, f in [0.5, 1) */
+    double m = nearbyint(f * 256.0);     /* 8 significant bits, ties to even */
+    if (m == 256.0) {
+        m = 128.0;
+        e2 += 1;
+    }
+    uint32_t bits = ((uint32_t)(e2 - 1 + 127) << 7) | ((uint32_t)m - 128u);
+    return (uint16_t)(signbit(v) ? (bits | 0x8000u) : bits);
+}
+
+void oracle_int4_quantize(int64_t N, int64_t K, const double *W, uint8_t *q, uint16_t *s)
+{
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t g = 0; g < K / 128; g++) {
+            const double *grp = W + n * K + g * 128;
+            double amax = 0.0;
+            for (int i = 0; i < 128; i++)
+                if (fabs(grp[i]) > amax) amax = fabs(grp[i]);
+            uint16_t sb = double_to_bf16_rne(amax / 7.0);
+            s[n * (K / 128) + g] = sb;
+            double sv = bf16_bits_to_double(sb);
+            for (int i = 0; i < 128; i += 2) {
+                int32_t c[2];
+                for (int j = 0; j < 2; j++) {
+                    double r = (sv == 0.0) ? 0.0 : nearbyint(grp[i + j] / sv);
+                    if (r > 7.0) r = 7.0;
+                    if (r < -8.0) r = -8.0;
+                    c[j] = (int32_t)r & 15;
+                }
+                q[n * (K / 2) + (g * 128 + i) / 2] = (uint8_t)(c[0] | (c[1] << 4));
             }
         }
     }

@@ -29,12 +29,18 @@
 extern "C" {
 #endif
 
-enum { ORACLE_FMT_BF16 = 0, ORACLE_FMT_NVFP4 = 1 };
+enum { ORACLE_FMT_BF16 = 0, ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_INT4 = 2 };
 
 /* One weight matrix of N rows by K columns, K contiguous.
    bf16:  data = uint16 bf16 bits [N][K].
    nvfp4: data = uint8 [N][K/2], two E2M1 codes per byte, low nibble = even column;
-          block_scale = E4M3 codes [N][K/16]; tensor_scale = one float. */
+          block_scale = E4M3 codes [N][K/16]; tensor_scale = one float.
+   int4:  data = uint8 [N][K/2], two signed 4-bit integers (two's complement, -8..7) per
+          byte, low nibble = even column; block_scale points at bf16 bits (uint16)
+          [N][K/128], one scale per 128 consecutive columns; tensor_scale unused.
+          The pages name an INT4 checkpoint without its layout (mrchatgpt.org
+          explainer, section 4; neoteo.com article); this symmetric, group-of-128,
+          bf16-scale form is the plainest common W4A16 reading. */
 typedef struct {
     int32_t format;
     const void *data;
@@ -52,6 +58,13 @@ typedef struct {
 double oracle_e2m1_value(uint32_t code);
 /* E4M3FN code (8 bits) -> value; 0x7F / 0xFF (NaN) return NaN. */
 double oracle_e4m3_value(uint32_t code);
+/* Signed 4-bit integer (two's complement nibble) -> value in -8..7. */
+double oracle_int4_value(uint32_t code);
+/* INT4 group quantiser (test data only): per row and group of 128 columns,
+   s = bf16(amax / 7) rounded to nearest even (0 if amax = 0), q = W / s rounded to
+   nearest even and clamped to -8..7 (0 where s = 0).  q uint8 [N][K/2], s bf16 bits
+   [N][K/128]; K % 128 == 0. */
+void oracle_int4_quantize(int64_t N, int64_t K, const double *W, uint8_t *q, uint16_t *s);
 /* Element (n, k) of a matrix, widened exactly to double. */
 double oracle_matrix_at(const oracle_matrix *m, int64_t K, int64_t n, int64_t k);
 

@@ -392,3 +392,88 @@ def test_zipf_constant_gives_half_the_assignments_to_16_experts():
     counts = np.bincount(ids.reshape(-1), minlength=E)
     share = np.sort(counts)[::-1][:16].sum() / (T * k)
     assert 0.49 <= share <= 0.51
+
+
+# ---------------------------------------------------------------- INT4 (W4A16 reading)
+def int4_nibbles_np(q):
+    """Independent INT4 decode: each nibble moved to the top of a byte and read as int8,
+    then an arithmetic right shift by 4 (two's complement sign extension by the CPU)."""
+    q = np.asarray(q, np.uint8)
+    lo = ((q & 15) << 4).astype(np.uint8).view(np.int8) >> 4
+    hi = (q & 0xF0).astype(np.uint8).view(np.int8) >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*q.shape[:-1], q.shape[-1] * 2).astype(np.float64)
+
+
+def int4_dequant_np(q, s_bits):
+    """Dense values of an INT4 matrix: nibbles times the bf16 group scale, the scale
+    decoded by torch's bfloat16 -> float64 conversion."""
+    vals = int4_nibbles_np(q)
+    sc = torch.from_numpy(np.ascontiguousarray(s_bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+    return vals * np.repeat(sc, 128, axis=-1)
+
+
+def test_int4_values_all_codes_vs_twos_complement():
+    vals = int4_nibbles_np(np.arange(16, dtype=np.uint8)[:, None])[:, 0]  # low nibbles
+    assert [oracle.int4_value(c) for c in range(16)] == list(vals)
+    assert vals.min() == -8 and vals.max() == 7
+
+
+def test_int4_matrix_element_layout_vs_numpy():
+    r = np.random.default_rng(7)
+    N, K = 3, 256
+    q = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    s = bf16_bits(r.uniform(0.001, 0.01, (N, K // 128)))
+    dense = int4_dequant_np(q, s)
+    for n in range(N):
+        for k in (0, 1, 2, 127, 128, 129, 254, 255):
+            assert oracle.matrix_at(oracle.FMT_INT4, q, s, K, n, k) == dense[n, k]
+
+
+def test_int4_quantiser_roundtrip_on_representable():
+    """A matrix that is exactly q * s with amax = 7 s per group quantises back to itself."""
+    r = np.random.default_rng(8)
+    N, K = 4, 384
+    s_bits = bf16_bits(r.uniform(1e-3, 1e-2, (N, K // 128)))
+    q_int = r.integers(-7, 8, (N, K))
+    q_int[:, ::128] = 7  # each group reaches amax = 7 s
+    W = q_int * np.repeat(bf16_val(s_bits), 128, axis=1)
+    q, s = oracle.int4_quantize(W)
+    np.testing.assert_array_equal(s, s_bits)
+    np.testing.assert_array_equal(int4_nibbles_np(q), q_int.astype(np.float64))
+
+
+def test_int4_quantiser_scale_and_error_bound():
+    r = np.random.default_rng(9)
+    N, K = 8, 512
+    W = r.normal(0, 0.02, (N, K))
+    W[0, :128] = 0.0  # an all-zero group: scale 0, codes 0
+    q, s = oracle.int4_quantize(W)
+    amax = np.abs(W).reshape(N, K // 128, 128).max(-1)
+    want = torch.from_numpy(amax / 7.0).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(s, want)
+    deq = int4_dequant_np(q, s)
+    sv = np.repeat(bf16_val(s), 128, axis=1)
+    assert np.all(np.abs(W - deq) <= sv / 2 + 1e-18)
+    assert np.all(int4_nibbles_np(q)[0, :128] == 0)
+
+
+def test_int4_experts_equal_dense_on_dequantised_weights():
+    T, H, I, E, k = 3, 128, 128, 4, 2
+    arrays = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        qs, ss = [], []
+        for e in range(E):
+            q, s = oracle.int4_quantize(rng.normal(0, 0.02, (N, K)))
+            qs.append(q); ss.append(s)
+        arrays["q_" + name] = np.stack(qs)
+        arrays["sb_" + name] = np.stack(ss)
+    routed = oracle.Experts(oracle.FMT_INT4, H, I, arrays)
+    x, Wr = _layer_inputs(T, H, I, E, k, seed=17)
+    out = oracle.moe_layer(x, Wr, routed, None, k)
+    for t in range(T):
+        xt = bf16_val(x[t])
+        ref = np.zeros(H)
+        for j, e in enumerate(out["ids"][t]):
+            g, u, d = (int4_dequant_np(arrays["q_" + n][e], arrays["sb_" + n][e]) for n in ("gate", "up", "down"))
+            ref += out["w"][t, j] * dense_swiglu(xt, g, u, d)
+        np.testing.assert_allclose(out["y"][t], ref, rtol=1e-12, atol=1e-15)
