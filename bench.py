@@ -11,7 +11,7 @@ HIP graph.  Inputs are seeded synthetic data drawn on the device before timing.
 Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant kernel (bytes or
 flops per launch over its measured duration) and the reference's single-core CPU rate on
 a bounded sample.  --config picks another workload: decode_t8, decode_t32, prefill,
-prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32, nvfp4_prefill, and the dense SwiGLU layer
+prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32, nvfp4_prefill, int4_t1, int4_t8, int4_t32, int4_prefill, and the dense SwiGLU layer
 (no router, I = 4096) at dense_t1, dense_t32, dense_prefill; chain_t1 and nvfp4_chain_t1
 run the single token through all 47 layers with one flint_moe_decode_chain call (token of
 layer l + 1 = bf16(x_l + y_l), formed in the kernel of layer l).
@@ -41,6 +41,11 @@ CONFIGS = {
     "nvfp4_t8": dict(T=8, fmt=1, layers=47, zipf=False),
     "nvfp4_t32": dict(T=32, fmt=1, layers=47, zipf=False),
     "nvfp4_prefill": dict(T=8192, fmt=1, layers=1, zipf=False),
+    # INT4 W4A16 (signed nibbles, one bf16 scale per 128 columns), same shapes
+    "int4_t1": dict(T=1, fmt=2, layers=47, zipf=False),
+    "int4_t8": dict(T=8, fmt=2, layers=47, zipf=False),
+    "int4_t32": dict(T=32, fmt=2, layers=47, zipf=False),
+    "int4_prefill": dict(T=8192, fmt=2, layers=1, zipf=False),
     # one token through the 47 layers in one flint_moe_decode_chain call, each layer's token =
     # bf16(previous token + previous layer's output) formed by the previous layer's kernel
     "chain_t1": dict(T=1, fmt=0, layers=47, zipf=False, chain=True),
@@ -60,7 +65,11 @@ def shape_of(cfg):
 
 
 def expert_bytes(fmt, H_, I_):
-    return 3 * I_ * H_ * 2 if fmt == 0 else 3 * (I_ * H_ // 2 + I_ * H_ // 16) + 3 * 4
+    if fmt == 0:
+        return 3 * I_ * H_ * 2
+    if fmt == 1:
+        return 3 * (I_ * H_ // 2 + I_ * H_ // 16) + 3 * 4
+    return 3 * (I_ * H_ // 2 + I_ * H_ // 64)
 METRIC = "MoE-layer tokens/s at T=1/8/32/8192; achieved HBM GB/s or MFMA % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "sparse_moe_transformer_wave_amd", "csrc")
@@ -129,6 +138,16 @@ def build_layer(torch, fm, dg, l, fmt, zipf, shp):
         else:
             d["weights"] = fm.Weights(0, d["gate"], d["up"], d["down"], d["gate"][E], d["up"][E],
                                       d["down"][E])
+    elif fmt == 2:
+        assert E > 0, "dense INT4 layers are not part of the benchmark"
+        for name, kind, N, K in kinds:
+            q = torch.empty((E + S, N, K // 2), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((E + S, N, K // 128), dtype=torch.int16, device="cuda")
+            dg.device_int4(q, sc, E + S, N, K, 0, dg.stream_id(l, kind, 0), dg.W_STD)
+            d["q_" + name], d["sc_" + name] = q, sc
+        d["weights"] = fm.Weights(
+            2, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
+            d["sc_gate"], d["sc_up"], d["sc_down"], d["sc_gate"][E], d["sc_up"][E], d["sc_down"][E])
     else:
         assert E > 0, "dense NVFP4 layers are not part of the benchmark"
         scratch = torch.empty(E + S, dtype=torch.int32, device="cuda")
@@ -158,6 +177,7 @@ def cpu_baseline(cfg, budget_s):
     from sparse_moe_transformer_wave_amd import datagen as dg
     H, I, E, TOPK, S = shape_of(cfg)
     nvfp4 = cfg["fmt"] == 1
+    int4 = cfg["fmt"] == 2
     # host quantisation costs ~1 s per expert: NVFP4 samples 2 tokens of one layer
     T = min(cfg["T"], 2) if nvfp4 else cfg["T"] if cfg["T"] <= 32 else 4
     n_layers = min(1 if nvfp4 else 8, cfg["layers"])
@@ -180,9 +200,13 @@ def cpu_baseline(cfg, budget_s):
                     q, sb, st = oracle.nvfp4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
                     for pre, v in (("q_", q), ("sb_", sb), ("st_", np.float32(st))):
                         arrays.setdefault(pre + name, []).append(v)
+                elif int4:
+                    q, sb = oracle.int4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
+                    for pre, v in (("q_", q), ("sb_", sb)):
+                        arrays.setdefault(pre + name, []).append(v)
                 else:
                     arrays.setdefault(name, []).append(dg.normal_bf16(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
-        fmt_o = oracle.FMT_NVFP4 if nvfp4 else oracle.FMT_BF16
+        fmt_o = oracle.FMT_NVFP4 if nvfp4 else oracle.FMT_INT4 if int4 else oracle.FMT_BF16
         routed = oracle.Experts(fmt_o, H, I, {k: np.stack(v[:-1]) for k, v in arrays.items()})
         shared = oracle.Experts(fmt_o, H, I, {k: np.stack(v[-1:]) for k, v in arrays.items()})
         layers.append((Wr, bias, local, routed, shared))
@@ -197,7 +221,8 @@ def cpu_baseline(cfg, budget_s):
         oracle.moe_tokens(routed, shared, x, lid, w)
         t_used += time.perf_counter() - t0
         done += 1
-    return cpu_result(T, done, n_layers, t_used, "full layer, NVFP4 weights" if nvfp4 else "full layer")
+    return cpu_result(T, done, n_layers, t_used, "full layer, NVFP4 weights" if nvfp4 else
+                      "full layer, INT4 weights" if int4 else "full layer")
 
 
 def host_cpu():
@@ -273,7 +298,7 @@ def main():
     shp = shape_of(cfg)
     H, I, E, TOPK, S = shp
     torch.cuda.init()
-    log("config %s: T=%d fmt=%s layers=%d" % (args.config, T, "bf16" if fmt == 0 else "nvfp4", L))
+    log("config %s: T=%d fmt=%s layers=%d" % (args.config, T, ("bf16", "nvfp4", "int4")[fmt], L))
     t0 = time.time()
     layers = [build_layer(torch, fm, dg, l, fmt, cfg["zipf"], shp) for l in range(L)]
     x = torch.empty((T, H), dtype=torch.int16, device="cuda")
@@ -389,11 +414,12 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "MoE-layer tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed_ms / K, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if fmt == 0 else "nvfp4-w4a16 (e2m1 weights x bf16 activations, fp32 accumulate)",
+        "dtype": ("bf16" if fmt == 0 else "nvfp4-w4a16 (e2m1 weights x bf16 activations, fp32 accumulate)"
+                  if fmt == 1 else "int4-w4a16 (int4 weights, bf16 scale per 128, x bf16 activations, fp32 accumulate)"),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tokens, drawn on device)",
         "config": {"workload": ("%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, "
                                 "SwiGLU, %s, %d distinct layers cycled%s"
-                                % (args.config, T, H, I, E, TOPK, S, "bf16" if fmt == 0 else "NVFP4",
+                                % (args.config, T, H, I, E, TOPK, S, ("bf16", "NVFP4", "INT4")[fmt],
                                    L, ", Zipf(1.1) logit bias" if cfg["zipf"] else
                                    ", chained: one flint_moe_decode_chain call per step, token of layer l + 1 = "
                                    "bf16(x_l + y_l)" if chain else "")) if E else

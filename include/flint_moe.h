@@ -67,7 +67,15 @@ enum {
        K share one E4M3FN scale; elements are E2M1 (bit 3 = sign, magnitudes
        0, .5, 1, 1.5, 2, 3, 4, 6), two per byte, the even column in the low nibble; one
        fp32 scale per (expert, matrix).  value = e2m1 * e4m3 * tensor_scale. */
-    FLINT_WFMT_NVFP4 = 1
+    FLINT_WFMT_NVFP4 = 1,
+    /* INT4 run as W4A16 (the pages name an INT4 checkpoint beside BF16 and NVFP4 without
+       its layout: mrchatgpt.org explainer, section 4; neoteo.com article).  Reading of
+       the format: signed 4-bit integers (two's complement, -8..7), two per byte, the even
+       column in the low nibble; one bf16 scale per row and group of 128 consecutive
+       columns along K; no zero point, no tensor scale.  value = q * scale.  The kernels
+       dequantise to bf16 (q * scale rounded once) for the bf16 products, except the
+       single-token path, which sums q * x per group in fp32 and scales the sum. */
+    FLINT_WFMT_INT4 = 2
 };
 
 /* ---- route flags ------------------------------------------------------------------- */
@@ -95,6 +103,9 @@ typedef struct {
             *_sf: E4M3 block scales, gate/up [E][I][H/16], down [E][H][I/16];
             gate_ts, up_ts, down_ts: fp32 [E] tensor scales (device memory);
             sh_ts: fp32 [3] = gate, up, down tensor scales of the shared expert.
+     INT4:  gate, up: uint8 [E][I][H/2]; down: uint8 [E][H][I/2]  (packed nibbles);
+            *_sf: bf16 group scales (uint16 bits), gate/up [E][I][H/128], down
+            [E][H][I/128]; every *_ts pointer NULL.
    Scale pointers must be NULL for BF16. */
 typedef struct {
     int32_t format;

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflint_moe.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_FORMAT, ERR_HIP = range(7)
-WFMT_BF16, WFMT_NVFP4 = 0, 1
+WFMT_BF16, WFMT_NVFP4, WFMT_INT4 = 0, 1, 2
 ROUTE_LOGITS_IN = 1
 CHAIN_RESIDUAL = 1
 

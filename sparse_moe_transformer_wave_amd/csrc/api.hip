@@ -51,7 +51,8 @@ int hip_status(hipError_t e)
 int check_weights(const flint_moe_desc *d, const flint_moe_weights *w)
 {
     if (!w) return FLINT_ERR_NULL;
-    if (w->format != FLINT_WFMT_BF16 && w->format != FLINT_WFMT_NVFP4) return FLINT_ERR_FORMAT;
+    if (w->format != FLINT_WFMT_BF16 && w->format != FLINT_WFMT_NVFP4 && w->format != FLINT_WFMT_INT4)
+        return FLINT_ERR_FORMAT;
     const bool dense = d->n_experts == 0;
     if (dense) {  // no routed experts: their pointers must be NULL
         const void *rp[] = {w->gate, w->up, w->down, w->gate_sf, w->up_sf, w->down_sf,
@@ -75,6 +76,19 @@ int check_weights(const flint_moe_desc *d, const flint_moe_weights *w)
             if (p) return FLINT_ERR_FORMAT;
         for (const void *p : shsc)
             if (p) return FLINT_ERR_FORMAT;
+    } else if (w->format == FLINT_WFMT_INT4) {  // group scales; no tensor scales
+        const void *gs[] = {w->gate_sf, w->up_sf, w->down_sf};
+        const void *shgs[] = {w->sh_gate_sf, w->sh_up_sf, w->sh_down_sf};
+        if (w->gate_ts || w->up_ts || w->down_ts || w->sh_ts) return FLINT_ERR_FORMAT;
+        for (const void *p : gs) {
+            if (!dense && !p) return FLINT_ERR_FORMAT;
+            if (!aligned16(p)) return FLINT_ERR_ALIGN;
+        }
+        for (const void *p : shgs) {
+            if (d->n_shared && !p) return FLINT_ERR_FORMAT;
+            if (!d->n_shared && p) return FLINT_ERR_FORMAT;
+            if (!aligned16(p)) return FLINT_ERR_ALIGN;
+        }
     } else {
         for (const void *p : sc)
             if (!dense && !p) return FLINT_ERR_FORMAT;
@@ -176,7 +190,7 @@ int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
 size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int32_t format)
 {
     if (check_desc(desc) != FLINT_OK || T_max < 0 || T_max > kMaxT) return 0;
-    if (format != FLINT_WFMT_BF16 && format != FLINT_WFMT_NVFP4) return 0;
+    if (format != FLINT_WFMT_BF16 && format != FLINT_WFMT_NVFP4 && format != FLINT_WFMT_INT4) return 0;
     return ws_layout(shape_of(desc), T_max).total;
 }
 

@@ -34,9 +34,16 @@ struct WMat {
     const float *ts_routed, *ts_shared;
 };
 struct WSet {
-    int fmt;  // 0 bf16, 1 nvfp4
+    int fmt;  // 0 bf16, 1 nvfp4, 2 int4 (sf_* = bf16 scale per 128 columns, no ts_*)
     WMat gate, up, down;
 };
+
+// Bytes of block / group scales per matrix row of K columns: NVFP4 one E4M3 byte per 16,
+// INT4 one bf16 per 128.
+__host__ __device__ constexpr size_t scale_row_bytes(int fmt, size_t K)
+{
+    return fmt == 1 ? K / 16 : fmt == 2 ? K / 64 : 0;
+}
 
 // Per-expert work description built on the device from the expert offsets.
 //   meta[0] = number of touched experts U' (routed with a token, then the shared one)
@@ -157,6 +164,41 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t q, float scale)
     u32x4 r{pack(v0), pack(v1), pack(v2), pack(v3)};
     if (scale == 0.f) r = u32x4{0u, 0u, 0u, 0u};
     return r;
+}
+
+// INT4 (W4A16): signed nibble i of a word (two's complement, low nibble first) as an int.
+__device__ __forceinline__ int int4_at(uint32_t q, int i)
+{
+    return (int)(q << (28 - 4 * i)) >> 28;
+}
+
+// Eight INT4 nibbles times their group scale, as 8 bf16 (4 words): each q * s is formed
+// in fp32 (exact: 4 x 8 significant bits) and rounded once to bf16 (nearest even, two at
+// a time by the packed conversion).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 dequant8_int4(uint32_t q, float scale)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const f32x2_t v = {(float)int4_at(q, 2 * i) * scale, (float)int4_at(q, 2 * i + 1) * scale};
+        const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+        w[i] = __builtin_bit_cast(uint32_t, b);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Eight INT4 nibbles as exact bf16 integers (4 words): a small integer converted to fp32
+// has at most 4 significant bits, so its upper half is its bf16 value.
+__device__ __forceinline__ u32x4 int4_bf16x8(uint32_t q)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        w[i] = __builtin_amdgcn_perm(__float_as_uint((float)int4_at(q, 2 * i + 1)),
+                                     __float_as_uint((float)int4_at(q, 2 * i)), 0x07060302u);
+    return u32x4{w[0], w[1], w[2], w[3]};
 }
 
 // Wave-wide reductions with DPP: xor-1 and xor-2 quad permutes, then the half-row and

@@ -134,6 +134,33 @@ __device__ __forceinline__ float dot32_nvfp4(u32x4 q, uint32_t sb2, const float 
     return blk[0] * e4m3_to_f32(sb2 & 0xffu) + blk[1] * e4m3_to_f32((sb2 >> 8) & 0xffu);
 }
 
+// One 16-byte INT4 chunk (32 signed nibbles of one 128-column group) against 32 fp32 x
+// values, times the group's bf16 scale.
+__device__ __forceinline__ float dot32_int4(u32x4 q, uint32_t sbits, const float *xv)
+{
+    float acc = 0.f;
+#pragma unroll
+    for (int wd = 0; wd < 4; wd++) {
+        const uint32_t qw = q[wd];
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc += (float)int4_at(qw, i) * xv[8 * wd + i];
+    }
+    return acc * bf2f(sbits & 0xffffu);
+}
+
+// Eight INT4 nibbles (one word) against 8 bf16 h values, in fp32.
+__device__ __forceinline__ float dot8_int4_bf16(uint32_t q, u32x4 h, float acc)
+{
+    const uint32_t h0 = h[0], h1 = h[1], h2 = h[2], h3 = h[3];
+    const uint32_t hv[4] = {h0, h1, h2, h3};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        acc += (float)int4_at(q, 2 * i) * bf2f(hv[i] & 0xffffu);
+        acc += (float)int4_at(q, 2 * i + 1) * bf2f(hv[i] >> 16);
+    }
+    return acc;
+}
+
 // Eight E2M1 codes (one word, low nibble first) against 8 bf16 h values: exact e2m1
 // values as bf16 pairs, then bf16 dot products.
 __device__ __forceinline__ float dot8_fp4_bf16(uint32_t q, u32x4 h, float acc)
@@ -194,14 +221,15 @@ __device__ __forceinline__ void row_issue(const D1Args &a, const WMat &m, int e,
 #pragma unroll
         for (int c = 0; c < kMaxXC; c++)
             if (lane + 64 * c < H / 8) r.v[c] = ld16(row + 8 * (lane + 64 * c));
-    } else {
+    } else {  // NVFP4: the lane's 32 k = 2 blocks; INT4: a quarter of one 128-column group
+        const size_t srow = scale_row_bytes(FMT, H);
         const uint8_t *row = mat_base(m, e, E, (size_t)I * H / 2) + (size_t)i * (H / 2);
-        const uint8_t *sf = mat_sf(m, e, E, (size_t)I * H / 16) + (size_t)i * (H / 16);
+        const uint8_t *sf = mat_sf(m, e, E, (size_t)I * srow) + (size_t)i * srow;
         if (lane < H / 32) {
             r.v[0] = ld16(row + 16 * lane);
-            r.sb = *reinterpret_cast<const uint16_t *>(sf + 2 * lane);
+            r.sb = *reinterpret_cast<const uint16_t *>(sf + (FMT == 1 ? 2 * lane : 2 * (lane >> 2)));
         }
-        r.ts = mat_ts(m, e, E);
+        r.ts = FMT == 1 ? mat_ts(m, e, E) : 1.f;
     }
 }
 
@@ -216,7 +244,7 @@ __device__ __forceinline__ float row_dot(const D1Args &a, const RowLoad<FMT> &r,
             if (lane + 64 * c < H / 8) acc = dot8_bf16(r.v[c], xb[c], acc);
         return wave_sum(acc);
     }
-    if (lane < H / 32) acc = dot32_nvfp4(r.v[0], r.sb, xf);
+    if (lane < H / 32) acc = FMT == 1 ? dot32_nvfp4(r.v[0], r.sb, xf) : dot32_int4(r.v[0], r.sb, xf);
     return wave_sum(acc) * r.ts;
 }
 
@@ -243,7 +271,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     const int n0 = b * rows_h;
     const int i0 = b * I / kG, npair = (b + 1) * I / kG - i0;  // gate/up rows of every expert
     const uint32_t tag = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    const size_t drow_bytes = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2 + I / 16;
+    const size_t drow_bytes = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2 + scale_row_bytes(FMT, I);
     const int cpb = (int)(rows_h * drow_bytes / 16);  // 16-byte chunks per slot block
     const int ngrp = (cpb + 63) / 64;                 // 64-chunk groups per slot block
 
@@ -277,7 +305,8 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
                 const uint8_t *src;
                 if (FMT == 0) src = mat_base(a.w.down, e, E, (size_t)H * I * 2) + (size_t)n0 * I * 2 + 16 * c;
                 else if (c < ncq) src = mat_base(a.w.down, e, E, (size_t)H * I / 2) + (size_t)n0 * (I / 2) + 16 * c;
-                else src = mat_sf(a.w.down, e, E, (size_t)H * I / 16) + (size_t)n0 * (I / 16) + 16 * (c - ncq);
+                else src = mat_sf(a.w.down, e, E, (size_t)H * scale_row_bytes(FMT, I)) +
+                           (size_t)n0 * scale_row_bytes(FMT, I) + 16 * (c - ncq);
                 lds_load16(src, dyn + ((size_t)j * cpb + 64 * g) * 16);
             }
         }
@@ -469,7 +498,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
                     for (int c = s; c < I / 8; c += 8)
                         acc = dot8_bf16(*reinterpret_cast<const u32x4 *>(row + 16 * c),
                                         *reinterpret_cast<const u32x4 *>(hj + 8 * c), acc);
-                } else {
+                } else if (FMT == 1) {
                     const uint8_t *qrow = blk + (size_t)n * (I / 2);
                     const uint8_t *sf = blk + (size_t)rows_h * (I / 2) + (size_t)n * (I / 16);
                     for (int c = s; c < I / 16; c += 8) {  // 16-element blocks: 8 code bytes, one scale
@@ -478,6 +507,16 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
                         float p = dot8_fp4_bf16(q0, *reinterpret_cast<const u32x4 *>(hj + 16 * c), 0.f);
                         p = dot8_fp4_bf16(q1, *reinterpret_cast<const u32x4 *>(hj + 16 * c + 8), p);
                         acc += p * e4m3_to_f32(sf[c]);
+                    }
+                } else {
+                    const uint8_t *qrow = blk + (size_t)n * (I / 2);
+                    const uint16_t *sf = reinterpret_cast<const uint16_t *>(blk + (size_t)rows_h * (I / 2) + (size_t)n * (I / 64));
+                    for (int c = s; c < I / 16; c += 8) {  // 16-element pieces; scale of group c / 8
+                        const u32x2 q = *reinterpret_cast<const u32x2 *>(qrow + 8 * c);
+                        const uint32_t q0 = q[0], q1 = q[1];
+                        float p = dot8_int4_bf16(q0, *reinterpret_cast<const u32x4 *>(hj + 16 * c), 0.f);
+                        p = dot8_int4_bf16(q1, *reinterpret_cast<const u32x4 *>(hj + 16 * c + 8), p);
+                        acc += p * bf2f(sf[c >> 3]);
                     }
                 }
             }
@@ -506,7 +545,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 // LDS for the down rows of one workgroup's H-slice, all k + S experts.
 static size_t d1_dyn_bytes(const Shape &s, int fmt)
 {
-    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + s.I / 16;
+    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + scale_row_bytes(fmt, s.I);
     return (size_t)(s.k + s.S) * (s.H / kG) * row;
 }
 
@@ -526,7 +565,7 @@ static int device_cus()
 
 bool decode1_supported(const Shape &s, int fmt)
 {
-    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + s.I / 16;
+    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + scale_row_bytes(fmt, s.I);
     const int rows_h = s.H / kG;
     return s.E >= 1 && s.H % kG == 0 && s.H <= 2048 &&                   // rows_h <= 8, x in 4 chunks per lane
            s.I % 32 == 0 && s.I <= 1024 && s.k <= kMaxK &&    // <= 4 gate/up pairs: one row per wave
@@ -539,7 +578,8 @@ static hipError_t launch_d1(const Shape &s, int fmt, const D1Args &a, hipStream_
     const size_t dyn = d1_dyn_bytes(s, fmt);
     // HIP on gfx950 takes up to the CU's 160 KB of LDS per workgroup without an opt-in.
     if (fmt == 0) decode1_kernel<0><<<kG, 512, dyn, st>>>(a);
-    else decode1_kernel<1><<<kG, 512, dyn, st>>>(a);
+    else if (fmt == 1) decode1_kernel<1><<<kG, 512, dyn, st>>>(a);
+    else decode1_kernel<2><<<kG, 512, dyn, st>>>(a);
     return hipGetLastError();
 }
 

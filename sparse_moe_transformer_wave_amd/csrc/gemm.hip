@@ -4,8 +4,8 @@
 // Benchmarking: the NVFP4 checkpoint barely changes the 8K-token prefill time), so the
 // expert FFNs run on bf16 MFMA with fp32 accumulation and LDS-staged tiles: bf16 weights
 // through a ring of K stages filled HBM -> LDS directly (gemm_bf16_kernel), NVFP4 weights
-// through registers, where they are dequantised, with a prefetch of the next K step
-// (grouped_gemm_kernel).
+// and INT4 weights through registers, where they are dequantised, with a prefetch of the
+// next K step (grouped_gemm_kernel).
 //
 // Work items come from the device plan: one item = (touched expert, 256-row tile of its
 // slots), so an expert of up to 256 rows streams its weights once.  Gate/up: A = the expert's tokens gathered from x, B = 32 gate rows and the same
@@ -93,9 +93,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
             brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * K * 2;
             bsf[j] = nullptr;
         } else {
-            const size_t mb = (size_t)H * I / 2, sb = (size_t)H * I / 16;
+            const size_t mb = (size_t)H * I / 2, srow = scale_row_bytes(FMT, K), sb = (size_t)(H * I / K) * srow;
             brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2);
-            bsf[j] = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * (K / 16);
+            bsf[j] = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * srow;
         }
     }
     const int schunk = tid & 7;
@@ -110,8 +110,12 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
             } else {
                 const int kk = k0 + schunk * 8;
                 uint32_t q = *reinterpret_cast<const uint32_t *>(brow[j] + kk / 2);
-                float s = e4m3_to_f32(bsf[j][kk / 16]);
-                rb[j] = dequant8(q, s);
+                if (FMT == 1) {
+                    rb[j] = dequant8(q, e4m3_to_f32(bsf[j][kk / 16]));
+                } else {
+                    const float s = bf2f(reinterpret_cast<const uint16_t *>(bsf[j])[kk / 128]);
+                    rb[j] = dequant8_int4(q, s);
+                }
             }
         }
     };
@@ -385,9 +389,12 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
         constexpr size_t lds = (size_t)kRingStages * 2 * 256 * 64;
         gemm_bf16_kernel<0, kRingStages><<<g1, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
-    } else {
+    } else if (w.fmt == 1) {
         grouped_gemm_kernel<0, 1><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         grouped_gemm_kernel<1, 1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+    } else {
+        grouped_gemm_kernel<0, 2><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        grouped_gemm_kernel<1, 2><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     }
     const int64_t nthreads = T * (s.H / 8);
     combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o,

@@ -123,10 +123,12 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
             }
         }
     } else {
-        // NVFP4: per 128-wide super-chunk a lane takes 32 consecutive k of its row (16
-        // bytes of codes, 2 block scales); MFMA j consumes the lane's k + 8j .. k + 8j + 7.
+        // NVFP4 / INT4: per 128-wide super-chunk a lane takes 32 consecutive k of its row
+        // (16 bytes of codes; NVFP4: 2 block scales, INT4: the one scale of the 128-column
+        // group); MFMA j consumes the lane's k + 8j .. k + 8j + 7.
+        const size_t srow = scale_row_bytes(FMT, H);
         const uint8_t *Q0 = expert_base(wm, e, E, (size_t)I * H / 2) + (size_t)(i0 + (r & 7)) * (H / 2);
-        const uint8_t *SF0 = expert_sf(wm, e, E, (size_t)I * H / 16) + (size_t)(i0 + (r & 7)) * (H / 16);
+        const uint8_t *SF0 = expert_sf(wm, e, E, (size_t)I * srow) + (size_t)(i0 + (r & 7)) * srow;
 #pragma unroll
         for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)tix[mt] * H;
         const int nsc = H / 128;
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
                     if (sc < nsc) {
                         const int kb = sc * 128 + g * 32;
                         qv[q][i] = ld16(Q0 + (size_t)q * 8 * (H / 2) + kb / 2);
-                        sb[q][i] = *reinterpret_cast<const uint16_t *>(SF0 + (size_t)q * 8 * (H / 16) + kb / 16);
+                        sb[q][i] = *reinterpret_cast<const uint16_t *>(SF0 + (size_t)q * 8 * srow +
+                                                                       (FMT == 1 ? kb / 16 : 2 * sc));
                     }
                 }
 #pragma unroll
@@ -161,14 +164,37 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
                 const int sc = s0 + 4 * i;
                 if (sc < nsc) {
 #pragma unroll
-                    for (int q = 0; q < RG; q++)
+                    for (int q = 0; q < RG; q++) {
+                        if (FMT == 1) {
 #pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            bf16x8 bv = as_bf16x8(dequant8(qv[q][i][j], e4m3_to_f32((sb[q][i] >> (8 * (j >> 1))) & 0xffu)));
+                            for (int j = 0; j < 4; j++) {
+                                bf16x8 bv = as_bf16x8(dequant8(qv[q][i][j], e4m3_to_f32((sb[q][i] >> (8 * (j >> 1))) & 0xffu)));
+#pragma unroll
+                                for (int mt = 0; mt < NMT; mt++)
+                                    if (NMT == 1 || mt < nmt) acc[q][mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, acc[q][mt]);
+                            }
+                        } else {
+                            // INT4: the super-chunk is one scale group and its 4 MFMAs
+                            // contract inside it, so they run on the exact integer codes
+                            // and the group scale of the lane's column (its own row)
+                            // multiplies their fp32 sum.
+                            f32x4 gsum[NMT];
+#pragma unroll
+                            for (int mt = 0; mt < NMT; mt++) gsum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int j = 0; j < 4; j++) {
+                                bf16x8 bv = as_bf16x8(int4_bf16x8(qv[q][i][j]));
+#pragma unroll
+                                for (int mt = 0; mt < NMT; mt++)
+                                    if (NMT == 1 || mt < nmt) gsum[mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, gsum[mt]);
+                            }
+                            const float sv = bf2f(sb[q][i]);
 #pragma unroll
                             for (int mt = 0; mt < NMT; mt++)
-                                if (NMT == 1 || mt < nmt) acc[q][mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, acc[q][mt]);
+                                acc[q][mt] = f32x4{acc[q][mt][0] + gsum[mt][0] * sv, acc[q][mt][1] + gsum[mt][1] * sv,
+                                                   acc[q][mt][2] + gsum[mt][2] * sv, acc[q][mt][3] + gsum[mt][3] * sv};
                         }
+                    }
                 }
             }
         }
@@ -265,9 +291,10 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                     acc[mt] = mfma16x16x32(as_bf16x8(has_tok[mt] ? ld16(hr[mt] + c0 * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u}), as_bf16x8(b), acc[mt]);
         }
     } else {
+        const size_t srow = scale_row_bytes(FMT, I);
         const uint8_t *Qd = expert_base(w.down, e, E, (size_t)H * I / 2) + (size_t)row * (I / 2);
-        const uint8_t *Sd = expert_sf(w.down, e, E, (size_t)H * I / 16) + (size_t)row * (I / 16);
-        ts = expert_ts(w.down, e, E);
+        const uint8_t *Sd = expert_sf(w.down, e, E, (size_t)H * srow) + (size_t)row * srow;
+        if (FMT == 1) ts = expert_ts(w.down, e, E);
         const int nsc = I / 128, se = nsc * (kw + 1) / KS;
         constexpr int NB = KS == 1 ? (NMT == 1 ? 6 : 3) : 2;
         for (int s0 = nsc * kw / KS; s0 < se; s0 += NB) {
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                 if (s0 + i < se) {
                     const int kb = (s0 + i) * 128 + g * 32;
                     q[i] = ld16(Qd + kb / 2);
-                    sb[i] = *reinterpret_cast<const uint16_t *>(Sd + kb / 16);
+                    sb[i] = *reinterpret_cast<const uint16_t *>(Sd + (FMT == 1 ? kb / 16 : 2 * (s0 + i)));
                 }
             }
 #pragma unroll
@@ -295,12 +322,30 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
 #pragma unroll
             for (int i = 0; i < NB; i++) {
                 if (s0 + i < se) {
+                    if (FMT == 1) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        bf16x8 bv = as_bf16x8(dequant8(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
+                        for (int j = 0; j < 4; j++) {
+                            bf16x8 bv = as_bf16x8(dequant8(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
+#pragma unroll
+                            for (int mt = 0; mt < NMT; mt++)
+                                if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, acc[mt]);
+                        }
+                    } else {  // INT4: integer codes per scale group, then the row's group scale
+                        f32x4 gsum[NMT];
+#pragma unroll
+                        for (int mt = 0; mt < NMT; mt++) gsum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            bf16x8 bv = as_bf16x8(int4_bf16x8(q[i][j]));
+#pragma unroll
+                            for (int mt = 0; mt < NMT; mt++)
+                                if (NMT == 1 || mt < nmt) gsum[mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, gsum[mt]);
+                        }
+                        const float sv = bf2f(sb[i]);
 #pragma unroll
                         for (int mt = 0; mt < NMT; mt++)
-                            if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i][j]), bv, acc[mt]);
+                            acc[mt] = f32x4{acc[mt][0] + gsum[mt][0] * sv, acc[mt][1] + gsum[mt][1] * sv,
+                                            acc[mt][2] + gsum[mt][2] * sv, acc[mt][3] + gsum[mt][3] * sv};
                     }
                 }
             }
@@ -431,8 +476,10 @@ hipError_t launch_gemv_forward(const Shape &s, const WSet &w, int64_t T, const u
 {
     if (w.fmt == 0)
         launch_stream<0>(s, w, T, x, topk_w, sa, ap, plan, h, o, y, st);
-    else
+    else if (w.fmt == 1)
         launch_stream<1>(s, w, T, x, topk_w, sa, ap, plan, h, o, y, st);
+    else
+        launch_stream<2>(s, w, T, x, topk_w, sa, ap, plan, h, o, y, st);
     return hipGetLastError();
 }
 

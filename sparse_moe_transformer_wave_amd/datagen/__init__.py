@@ -176,7 +176,8 @@ def _D():
         L.flint_gen_normal_bf16.argtypes = [vp, i64, i64, u64, u64, d, vp]
         L.flint_gen_normal_f32.argtypes = [vp, i64, u64, u64, d, vp]
         L.flint_gen_nvfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, u64, u64, d, vp]
-        for f in ("flint_gen_normal_bf16", "flint_gen_normal_f32", "flint_gen_nvfp4"):
+        L.flint_gen_int4.argtypes = [vp, vp, i64, i64, i64, u64, u64, d, vp]
+        for f in ("flint_gen_normal_bf16", "flint_gen_normal_f32", "flint_gen_nvfp4", "flint_gen_int4"):
             getattr(L, f).restype = ctypes.c_int
         _dev = L
     return _dev
@@ -199,6 +200,14 @@ def device_normal_f32(t, seed: int, stream: int, std: float):
     rc = _D().flint_gen_normal_f32(t.data_ptr(), t.numel(), seed, stream, std, _cur_stream())
     if rc:
         raise RuntimeError("flint_gen_normal_f32 failed: %d" % rc)
+
+
+def device_int4(q, sc, n_mat: int, N: int, K: int, seed: int, stream0: int, std: float):
+    """INT4 pool on the device: codes q uint8 [n_mat][N][K/2], bf16 group scales sc
+    (int16 tensor) [n_mat][N][K/128]."""
+    rc = _D().flint_gen_int4(q.data_ptr(), sc.data_ptr(), n_mat, N, K, seed, stream0, std, _cur_stream())
+    if rc:
+        raise RuntimeError("flint_gen_int4 failed: %d" % rc)
 
 
 def device_nvfp4(q, sf, ts, scratch, n_mat: int, N: int, K: int, seed: int, stream0: int,

@@ -52,13 +52,17 @@ class Case:
                 if wscale is not None:
                     sd = dg.f32_to_bf16_bits(dg.bf16_bits_to_f32(sd) * wscale)
                 self.host_sh = {"gate": sg[None], "up": su[None], "down": sd[None]}
-        else:
+        elif fmt == fm.WFMT_NVFP4:
             self.host = self._nvfp4_set(ex, E)
             if S:
                 self.host_sh = self._nvfp4_set([E], 1, offset=E)
-        self.routed = oracle.Experts(oracle.FMT_BF16 if fmt == 0 else oracle.FMT_NVFP4, H, I, self.host)
-        self.shared = oracle.Experts(oracle.FMT_BF16 if fmt == 0 else oracle.FMT_NVFP4, H, I,
-                                     self.host_sh) if S else None
+        else:
+            self.host = self._int4_set(ex, E)
+            if S:
+                self.host_sh = self._int4_set([E], 1, offset=E)
+        ofmt = {fm.WFMT_BF16: oracle.FMT_BF16, fm.WFMT_NVFP4: oracle.FMT_NVFP4, fm.WFMT_INT4: oracle.FMT_INT4}[fmt]
+        self.routed = oracle.Experts(ofmt, H, I, self.host)
+        self.shared = oracle.Experts(ofmt, H, I, self.host_sh) if S else None
         self.logits_in = logits_in
 
     def _bf16(self, e):
@@ -81,6 +85,19 @@ class Case:
             out["q_" + name], out["sb_" + name], out["st_" + name] = q, sb, st
         return out
 
+    def _int4_set(self, ex, n, offset=0):
+        H, I, s, L = self.H, self.I, self.seed, self.layer
+        out = {}
+        for name, kind, (N, K) in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
+                                   ("down", dg.KIND_DOWN, (H, I))):
+            q = np.zeros((n, N, K // 2), np.uint8)
+            sb = np.zeros((n, N, K // 128), np.uint16)
+            for e in ex:
+                W = dg.normal_f64((N, K), s, dg.stream_id(L, kind, e), dg.W_STD)
+                q[e - offset], sb[e - offset] = oracle.int4_quantize(W)
+            out["q_" + name], out["sb_" + name] = q, sb
+        return out
+
     # ------------------------------------------------------------------ device side
     def upload(self):
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -92,6 +109,15 @@ class Case:
             hs = {k: dev(v.view(np.int16)) for k, v in self.host_sh.items()} if self.S else {}
             self.weights = fm.Weights(fm.WFMT_BF16, h["gate"], h["up"], h["down"],
                                       hs.get("gate"), hs.get("up"), hs.get("down"))
+            self._keep = (h, hs)
+        elif self.fmt == fm.WFMT_INT4:
+            h = {k: dev(v.view(np.int16) if v.dtype == np.uint16 else v) for k, v in self.host.items()}
+            hs = {k: dev(v.view(np.int16) if v.dtype == np.uint16 else v) for k, v in self.host_sh.items()} if self.S else {}
+            self.weights = fm.Weights(
+                fm.WFMT_INT4, h["q_gate"], h["q_up"], h["q_down"],
+                hs.get("q_gate"), hs.get("q_up"), hs.get("q_down"),
+                h["sb_gate"], h["sb_up"], h["sb_down"],
+                hs.get("sb_gate"), hs.get("sb_up"), hs.get("sb_down"))
             self._keep = (h, hs)
         else:
             h = {k: dev(v) for k, v in self.host.items()}

@@ -167,3 +167,25 @@ def test_decode_chain_validation():
     nv = fm.Weights(fm.WFMT_NVFP4, A, A, A, A, A, A, A, A, A, A, A, A, A, A, A, A)
     assert chain([good, (nv, A, None)]) == fm.ERR_FORMAT  # formats differ
     assert chain([good], nb=need - 1) == fm.ERR_WORKSPACE
+
+
+def test_int4_weight_validation():
+    """INT4: group scales required (shared ones iff n_shared), tensor scales forbidden."""
+    d = fm.desc(2048, 768)
+    need = fm.workspace_bytes(d, 8, fm.WFMT_INT4)
+    assert need > 0
+    ok = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, A, A, A, A, A, A)
+    assert _forward(d, ok.c_struct(), 8, nb=need - 1) == fm.ERR_WORKSPACE
+    bad_ts = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, A, A, A, A, A, A, gate_ts=A)
+    assert _forward(d, bad_ts.c_struct(), 8, nb=need) == fm.ERR_FORMAT
+    bad_sh_ts = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, A, A, A, A, A, A, sh_ts=A)
+    assert _forward(d, bad_sh_ts.c_struct(), 8, nb=need) == fm.ERR_FORMAT
+    no_sf = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, None, A, A, A, A, A)
+    assert _forward(d, no_sf.c_struct(), 8, nb=need) == fm.ERR_FORMAT
+    no_sh_sf = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, A, A, A, None, A, A)
+    assert _forward(d, no_sh_sf.c_struct(), 8, nb=need) == fm.ERR_FORMAT
+    mis = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, A, MIS, A, A, A, A)
+    assert _forward(d, mis.c_struct(), 8, nb=need) == fm.ERR_ALIGN
+    d0 = fm.desc(2048, 768, n_shared=0)
+    sh_sf_without_shared = fm.Weights(fm.WFMT_INT4, A, A, A, None, None, None, A, A, A, A, None, None)
+    assert _forward(d0, sh_sf_without_shared.c_struct(), 8, nb=need) == fm.ERR_FORMAT

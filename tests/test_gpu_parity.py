@@ -337,3 +337,34 @@ def test_chain_tiny_nvfp4():
 @pytest.mark.parametrize("fmt", [fm.WFMT_BF16, fm.WFMT_NVFP4])
 def test_chain_full(fmt):
     _chain_check(2048, 768, 256, 6, fmt, 3, True, predict_experts=True)
+
+
+# ---------------------------------------------------------------- INT4 (W4A16)
+@pytest.mark.parametrize("T", [1, 8, 32, 40, 200])
+def test_tiny_int4(T):
+    _parity(Case(T, 256, 128, 256, 6, fmt=fm.WFMT_INT4))
+
+
+def test_int4_single_token_launch():
+    """H = 1024, I = 768: the single-token persistent launch with INT4 rows (a workgroup's
+    down rows, codes plus group scales, fill whole 16-byte chunks)."""
+    _parity(Case(1, 1024, 768, 256, 6, fmt=fm.WFMT_INT4))
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_full_decode_int4(T):
+    _parity(_full_case(T, fmt=fm.WFMT_INT4))
+
+
+def test_full_prefill_int4_8192():
+    H, I, E, k, T = 2048, 768, 256, 6, 8192
+    toks = np.unique(np.concatenate([np.arange(0, T, 523), [T - 1]])).astype(np.int64)
+    x = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), 1.0)
+    Wr = dg.normal_f32((E, H), 0, dg.stream_id(0, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+    ids = oracle.select(oracle.router(x[toks], Wr), k)
+    c = Case(T, H, I, E, k, fmt=fm.WFMT_INT4, experts=sorted(set(ids.reshape(-1).tolist())))
+    _parity(c, tokens=toks)
+
+
+def test_chain_full_int4():
+    _chain_check(2048, 768, 256, 6, fm.WFMT_INT4, 3, True, predict_experts=True)
