@@ -147,7 +147,8 @@ WsLayout ws_layout(const Shape &s, int64_t T)
     L.offsets = take((size_t)(s.E + 1) * 4);
     L.sa = take(TK * 4);
     L.ap = take(TK * 4);
-    L.plan = take((size_t)(4 + 3 * (s.E + 1) + L.max_items) * 4);
+    L.plan = take((size_t)(4 + 3 * plan_unit_capacity(s.E, s.k, s.S, T) + L.max_items) * 4);
+    L.plan_units = (int)plan_unit_capacity(s.E, s.k, s.S, T);
     L.hist = take(((TK + 1023) / 1024) * (size_t)s.E * 4);
     L.h = take(slots * s.I * 4);
     L.o = take(slots * s.H * 4);
@@ -157,13 +158,14 @@ WsLayout ws_layout(const Shape &s, int64_t T)
 
 Plan plan_view(void *ws, const WsLayout &L, const Shape &s)
 {
+    (void)s;
     int *b = (int *)((char *)ws + L.plan);
     Plan p;
     p.meta = b;
     p.touched = b + 4;
-    p.tbase = p.touched + (s.E + 1);
-    p.tcount = p.tbase + (s.E + 1);
-    p.items = p.tcount + (s.E + 1);
+    p.tbase = p.touched + L.plan_units;
+    p.tcount = p.tbase + L.plan_units;
+    p.items = p.tcount + L.plan_units;
     return p;
 }
 

@@ -22,6 +22,15 @@ struct Shape {
 // Streaming (GEMV-like) path handles T up to this many tokens; larger T uses the
 // grouped GEMM.  Two 16-token MFMA row tiles cover it.
 constexpr int kGemvMaxT = 32;
+constexpr int kUnitRows = 16;  // rows (tokens) per streaming work unit: one MFMA token tile
+
+// Work units the plan may list: touched experts, plus the extra units of experts split
+// into kUnitRows-row pieces on the streaming path (T <= kGemvMaxT).
+__host__ __device__ inline int64_t plan_unit_capacity(int E, int k, int S, int64_t T)
+{
+    const int64_t ts = T < kGemvMaxT ? T : kGemvMaxT;
+    return (int64_t)E + S + (ts * k + kUnitRows - 1) / kUnitRows + (int64_t)S * ((ts + kUnitRows - 1) / kUnitRows);
+}
 // Grouped GEMM tile: BM rows (tokens) x 256 B-rows x 64 K.
 constexpr int kGemmBM = 256;
 
@@ -46,11 +55,12 @@ __host__ __device__ constexpr size_t scale_row_bytes(int fmt, size_t K)
 }
 
 // Per-expert work description built on the device from the expert offsets.
-//   meta[0] = number of touched experts U' (routed with a token, then the shared one)
+//   meta[0] = number of units U' (touched routed experts in ascending id, then the shared
+//             one; on the streaming path an expert of more than kUnitRows rows is split
+//             into consecutive units of at most kUnitRows rows)
 //   meta[1] = number of grouped-GEMM items
-//   touched[u], tbase[u] (first slot), tcount[u] (rows) for u < U'
+//   touched[u] (expert), tbase[u] (first slot), tcount[u] (rows) for u < U'
 //   items[i] = (u << 16) | m_tile
-//   counters[H/16] completion counters of the decode down pass (zeroed by the planner)
 struct Plan {
     int *meta;
     int *touched, *tbase, *tcount;
@@ -63,6 +73,7 @@ struct WsLayout {
     size_t sync, plan, hist, h, o;
     size_t total;
     int max_items;
+    int plan_units;  // capacity of the plan's touched / tbase / tcount arrays
 };
 WsLayout ws_layout(const Shape &s, int64_t T);
 Plan plan_view(void *ws, const WsLayout &L, const Shape &s);

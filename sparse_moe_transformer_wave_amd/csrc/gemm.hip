@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
         const int rr = (tid + NT * j) >> 3;
         const int ri = min(rr, valid - 1);
         if (MODE == 0) {
-            const int tok = sh ? m0 + ri : sa[base + m0 + ri] / k;
+            const int tok = sh ? base - T * k + m0 + ri : sa[base + m0 + ri] / k;
             arow[j] = asrc + (size_t)tok * H;
         } else {
             arow[j] = asrc + (size_t)(base + m0 + ri) * I;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
     {
         const int ri = min(crow, valid - 1);
         if (MODE == 0) {
-            const int tok = sh ? m0 + ri : sa[base + m0 + ri] / k;
+            const int tok = sh ? base - T * k + m0 + ri : sa[base + m0 + ri] / k;
             ap_ = asrc + (size_t)tok * H + 8 * cchunk;
         } else {
             ap_ = asrc + (size_t)(base + m0 + ri) * I + 8 * cchunk;

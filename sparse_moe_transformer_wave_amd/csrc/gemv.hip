@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 #pragma unroll
     for (int mt = 0; mt < NMT; mt++) {
         const int idx = min(mt * 16 + r, cnt - 1);
-        tix[mt] = (e == E) ? idx : sa_in[base + idx] / k;  // token of the A row (k >= 1 if routed)
+        // token of the A row: the shared expert's slot T k + t holds token t (a unit of it
+        // may start past T k); routed slots hold assignments t k + j (k >= 1)
+        tix[mt] = (e == E) ? base - T * k + idx : sa_in[base + idx] / k;
     }
     const uint16_t *xr[NMT];
     const int nmt = (cnt + 15) >> 4;
@@ -449,22 +451,23 @@ static void launch_down(const Shape &s, const WSet &w, int maxU, int cls, const 
         gemv_down_kernel<FMT, NMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, cls, w, h, plan, o);
 }
 
-// T <= 16: every unit fits one token tile.  Larger T: units of at most 16 tokens (all but
-// the shared expert, as a rule) run the one-tile kernels, the others the two-tile ones.
+// With routed experts the plan lists units of at most 16 tokens (an expert with more is
+// split; in practice the shared expert once T > 16), so one launch of the one-tile
+// kernels covers every unit.  A dense layer (E = 0) keeps its single unit whole, so its
+// weights are read once: the two-tile kernels for T > 16.
 template <int FMT>
 static void launch_stream(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                           const float *topk_w, const int32_t *sa, const int32_t *ap,
                           const Plan &plan, uint16_t *h, float *o, uint16_t *y, hipStream_t st)
 {
-    const int maxU = (int)std::min<int64_t>(T * s.k, s.E) + s.S;
-    if (T <= 16) {
+    const int maxU = (int)(std::min<int64_t>(T * s.k, s.E) + (T * s.k + kUnitRows - 1) / kUnitRows +
+                           (int64_t)s.S * ((T + kUnitRows - 1) / kUnitRows));
+    if (s.E > 0 || T <= 16) {
         launch_gateup<FMT, 1>(s, w, T, maxU, 0, x, sa, plan, h, st);
         launch_down<FMT, 1>(s, w, maxU, 0, h, plan, o, st);
     } else {
-        launch_gateup<FMT, 1>(s, w, T, maxU, 1, x, sa, plan, h, st);
-        launch_gateup<FMT, 2>(s, w, T, maxU, 2, x, sa, plan, h, st);
-        launch_down<FMT, 1>(s, w, maxU, 1, h, plan, o, st);
-        launch_down<FMT, 2>(s, w, maxU, 2, h, plan, o, st);
+        launch_gateup<FMT, 2>(s, w, T, 1, 0, x, sa, plan, h, st);
+        launch_down<FMT, 2>(s, w, 1, 0, h, plan, o, st);
     }
     const int nthreads = (int)T * (s.H / 8);
     gemv_combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o, topk_w, ap, y);

@@ -41,25 +41,34 @@ struct PlanScratch {
 };
 
 // Build the plan from per-expert counts and offsets held in LDS.  Touched experts are
-// listed in ascending id, the shared expert (id E, all T tokens) last.
+// listed in ascending id, the shared expert (id E, all T tokens) last.  For the streaming
+// path (T <= kGemvMaxT, routed experts present) an expert with more than kUnitRows rows
+// is listed as several units of at most kUnitRows rows, so one token-tile width serves
+// every unit (the shared expert's weights are then read once per unit).
 __device__ void build_plan(int T, int E, int k, int S, int H, const int *cnt, const int *off,
                            const Plan &p, PlanScratch &ps)
 {
     const int tid = threadIdx.x, bd = blockDim.x;
     const int n = E + S;
-    for (int e = tid; e < n; e += bd) ps.flag[e] = (e < E) ? (cnt[e] > 0) : (T > 0);
+    const bool split = T <= kGemvMaxT && E > 0;
+    for (int e = tid; e < n; e += bd) {
+        const int rows = (e < E) ? cnt[e] : T;
+        ps.flag[e] = rows <= 0 ? 0 : split ? (rows + kUnitRows - 1) / kUnitRows : 1;
+    }
     __syncthreads();
     if (tid < 64) wave0_exclusive_scan(ps.flag, ps.idx, n);
     __syncthreads();
     const int nT = ps.idx[n];
     for (int e = tid; e < n; e += bd) {
-        if (!ps.flag[e]) continue;
-        int u = ps.idx[e];
-        int rows = (e < E) ? cnt[e] : T;
-        p.touched[u] = e;
-        p.tbase[u] = (e < E) ? off[e] : T * k;
-        p.tcount[u] = rows;
-        ps.nt[u] = (rows + kGemmBM - 1) / kGemmBM;
+        const int rows = (e < E) ? cnt[e] : T, base = (e < E) ? off[e] : T * k;
+        for (int c = 0; c < ps.flag[e]; c++) {
+            const int u = ps.idx[e] + c;
+            const int r = split ? min(kUnitRows, rows - kUnitRows * c) : rows;
+            p.touched[u] = e;
+            p.tbase[u] = base + (split ? kUnitRows * c : 0);
+            p.tcount[u] = r;
+            ps.nt[u] = (r + kGemmBM - 1) / kGemmBM;
+        }
     }
     __syncthreads();
     if (tid < 64) wave0_exclusive_scan(ps.nt, ps.base, nT);
@@ -187,17 +196,24 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
         sa[pos] = tid;
         ap[tid] = pos;
     }
+    // units of at most kUnitRows rows (as in build_plan's streaming case)
     const int nf = E + S;
-    if (tid < nf) g.flag[tid] = tid < E ? (g.cnt[tid] > 0) : 1;
+    if (tid < nf) {
+        const int rows = tid < E ? g.cnt[tid] : T;
+        g.flag[tid] = (rows + kUnitRows - 1) / kUnitRows;
+    }
     __syncthreads();
     if (tid < 64) wave0_exclusive_scan(g.flag, g.idx, nf);
     __syncthreads();
-    if (tid < nf && g.flag[tid]) {
-        const int u = g.idx[tid];
-        p.touched[u] = tid;
-        p.tbase[u] = tid < E ? g.off[tid] : T * k;
-        p.tcount[u] = tid < E ? g.cnt[tid] : T;
-        p.items[u] = u << 16;
+    if (tid < nf) {
+        const int rows = tid < E ? g.cnt[tid] : T, base = tid < E ? g.off[tid] : T * k;
+        for (int c = 0; c < g.flag[tid]; c++) {
+            const int u = g.idx[tid] + c;
+            p.touched[u] = tid;
+            p.tbase[u] = base + kUnitRows * c;
+            p.tcount[u] = min(kUnitRows, rows - kUnitRows * c);
+            p.items[u] = u << 16;
+        }
     }
     if (tid == 0) {
         p.meta[0] = g.idx[nf];

@@ -50,7 +50,9 @@ def test_tiny_three_call_path(T):
 
 @pytest.mark.parametrize("T,E,k,S,renorm", [
     (5, 1, 1, 0, 1), (40, 1, 1, 1, 1), (7, 8, 8, 1, 1), (50, 8, 8, 0, 1),
-    (9, 16, 4, 0, 0), (64, 16, 4, 1, 0), (3, 256, 8, 1, 1)])
+    (9, 16, 4, 0, 0), (64, 16, 4, 1, 0), (3, 256, 8, 1, 1),
+    # streaming path with experts of more than 16 tokens (split into 16-row units)
+    (32, 8, 8, 1, 1), (24, 4, 4, 0, 1), (17, 2, 2, 1, 0)])
 def test_edge_shapes(T, E, k, S, renorm):
     _parity(Case(T, 256, 128, E, k, S=S, renorm=renorm))
 
