@@ -429,13 +429,13 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(int T, int H, int k, 
     *reinterpret_cast<u32x4 *>(y + (size_t)t * H + c) = outv;
 }
 
-// Gate/up, row groups per wave: 2 for bf16 with one token tile, else 1 (NVFP4 dequantisation
-// already keeps a wave busy: more groups only raise its register count).
+// Gate/up, row groups per wave: 2 for bf16 and INT4 with one token tile, else 1 (NVFP4
+// dequantisation already keeps a wave busy: a second group measured slower).
 template <int FMT, int NMT>
 static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, int cls, const uint16_t *x,
                           const int32_t *sa, const Plan &plan, uint16_t *h, hipStream_t st)
 {
-    constexpr int RG = FMT == 0 && NMT == 1 ? 2 : 1;
+    constexpr int RG = FMT != 1 && NMT == 1 ? 2 : 1;
     const unsigned grid = (unsigned)(maxU * (s.I / (8 * RG)));
     gemv_gateup_kernel<FMT, NMT, RG><<<grid, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, w, x, sa, plan, h);
 }

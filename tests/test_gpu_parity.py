@@ -370,3 +370,42 @@ def test_full_prefill_int4_8192():
 
 def test_chain_full_int4():
     _chain_check(2048, 768, 256, 6, fm.WFMT_INT4, 3, True, predict_experts=True)
+
+
+# ---------------------------------------------------------------- HIP graph replay
+@pytest.mark.parametrize("T", [1, 8, 100])
+def test_graph_replays_match_eager(T):
+    """The layer captured in a HIP graph (as the benchmark runs it), replayed several times
+    with eager calls on the same workspace in between: every replay gives the eager
+    result bit for bit (the single-token launch's tags come from the launch counter in
+    device memory, so replays never reuse a tag; the small-batch arrival counter re-arms
+    itself; nothing is cleared with a memset node)."""
+    c = Case(T, 256, 128, 256, 6, layer=2).upload()
+    ws = c.workspace()
+    y_eager = torch.zeros((T, 256), dtype=torch.int16, device="cuda")
+    fm.layer(c.desc, c.weights, T, c.d_x, c.d_Wr, None, y_eager, ws)
+    torch.cuda.synchronize()
+    ref = y_eager.clone()
+    y_graph = torch.zeros_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fm.layer(c.desc, c.weights, T, c.d_x, c.d_Wr, None, y_graph, ws)  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            fm.layer(c.desc, c.weights, T, c.d_x, c.d_Wr, None, y_graph,
+                     ws, stream=torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        y_graph.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph, ref), "replay %d differs from the eager result" % rep
+        fm.layer(c.desc, c.weights, T, c.d_x, c.d_Wr, None, y_eager, ws)  # eager work in between
+        torch.cuda.synchronize()
+        assert torch.equal(y_eager, ref)
+    if T == 1:
+        head = ws[:8].view(torch.int32).cpu().numpy()
+        assert head[1] == 0, "a wait timed out"
