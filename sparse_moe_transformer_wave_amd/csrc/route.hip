@@ -40,15 +40,26 @@ __global__ __launch_bounds__(256) void router_small_kernel(int T, int H, int E,
 // x . w = x . hi + x . mid + x . lo up to fp32 summation rounding (the split is the
 // three-term bf16 decomposition of an fp32 operand; Henry, Tang and Heinecke,
 // "Leveraging the bfloat16 artificial intelligence datatype for higher-precision
-// computations", ARITH 2019).  Tile: 128 tokens x 64 experts x 64 K per 256-thread
-// workgroup; each wave owns 32 tokens x 64 experts (2 x 4 MFMA tiles, 3 MFMAs each).
+// computations", ARITH 2019).  Tile: 128 tokens x 64 experts x 64 K per 512-thread
+// workgroup (two waves per SIMD); wave w owns 16 experts (w % 4) x 64 tokens (w / 4)
+// (4 MFMA tiles, 3 MFMAs each), so a wave reads its 3 weight-part fragments once per
+// 32-K step and its 4 token fragments serve all of them (the weight parts are the larger
+// operand: splitting the tile by tokens only made every wave re-read all 3 x 64 expert
+// rows from LDS).  Global loads run two K steps ahead in registers (stage k + 2 is
+// fetched while stage k is multiplied and stage k + 1 waits to be split into LDS).
 namespace {
-constexpr int RBM = 128, RBN = 64, RBK = 32, RLD = RBK + 8;
+constexpr int RBM = 128, RBN = 64, RBK = 64, RLD = RBK + 8;
 
 __device__ __forceinline__ uint32_t trunc_bf16(float v) { return __float_as_uint(v) >> 16; }
+
+constexpr int RNT = 512;  // threads per workgroup
+struct RouterStage {
+    u32x4 a[2];   // token chunks tid + 512 j: row c / 8, 8 bf16 at column 8 (c % 8)
+    float4 b[2];  // weight chunks tid + 512 j: row c / 16, 4 fp32 at column 4 (c % 16)
+};
 }  // namespace
 
-__global__ __launch_bounds__(256) void router_mfma_kernel(int T, int H, int E,
+__global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
                                                           const uint16_t *__restrict__ x,
                                                           const float *__restrict__ Wr,
                                                           const float *__restrict__ bias,
@@ -58,35 +69,31 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int H, int E,
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][RBN][RLD];
     const int t0 = blockIdx.x * RBM, e0 = blockIdx.y * RBN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    f32x4 acc[2][4];
+    const int we = wave & 3, wt = wave >> 2;  // expert group, token half
+    f32x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // staging: A 128 rows x 4 chunks of 8 bf16 (2 per thread); B 64 rows x 8 float4 (2 per thread)
+    for (int i = 0; i < 4; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t *xa[2];
     const float *wb[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-        const int c = tid + 256 * j;
-        xa[j] = x + (size_t)min(t0 + (c >> 2), T - 1) * H + (c & 3) * 8;
-        wb[j] = Wr + (size_t)min(e0 + (c >> 3), E - 1) * H + (c & 7) * 4;
+        const int c = tid + RNT * j;
+        xa[j] = x + (size_t)min(t0 + (c >> 3), T - 1) * H + (c & 7) * 8;
+        wb[j] = Wr + (size_t)min(e0 + (c >> 4), E - 1) * H + (c & 15) * 4;
     }
-    u32x4 ra[2];
-    float4 rb[2];
-    auto gload = [&](int k0) {
+    auto gload = [&](int k0, RouterStage &st) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            ra[j] = *reinterpret_cast<const u32x4 *>(xa[j] + k0);
-            rb[j] = *reinterpret_cast<const float4 *>(wb[j] + k0);
+            st.a[j] = *reinterpret_cast<const u32x4 *>(xa[j] + k0);
+            st.b[j] = *reinterpret_cast<const float4 *>(wb[j] + k0);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, const RouterStage &st) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int c = tid + 256 * j;
-            *reinterpret_cast<u32x4 *>(&As[buf][c >> 2][(c & 3) * 8]) = ra[j];
-            const float vv[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
+            const int c = tid + RNT * j;
+            *reinterpret_cast<u32x4 *>(&As[buf][c >> 3][(c & 7) * 8]) = st.a[j];
+            const float vv[4] = {st.b[j].x, st.b[j].y, st.b[j].z, st.b[j].w};
             uint32_t hi[4], mid[4], lo[4];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
@@ -96,47 +103,55 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int H, int E,
                 const float r2 = r1 - __uint_as_float(mid[q] << 16);
                 lo[q] = f2bf(r2);
             }
-            const int row = c >> 3, col = (c & 7) * 4;
+            const int row = c >> 4, col = (c & 15) * 4;
             *reinterpret_cast<u32x2 *>(&Bs[buf][0][row][col]) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
             *reinterpret_cast<u32x2 *>(&Bs[buf][1][row][col]) = u32x2{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16)};
             *reinterpret_cast<u32x2 *>(&Bs[buf][2][row][col]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
         }
     };
-    const int nk = H / RBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * RBK);
-        bf16x8 af[2];
+    auto compute = [&](int buf) {
 #pragma unroll
-        for (int ms = 0; ms < 2; ms++)
-            af[ms] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&As[buf][wave * 32 + ms * 16 + r][g * 8]));
+        for (int kk = 0; kk < RBK / 32; kk++) {
+            bf16x8 bfr[3];
 #pragma unroll
-        for (int part = 0; part < 3; part++) {
+            for (int part = 0; part < 3; part++)
+                bfr[part] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bs[buf][part][we * 16 + r][kk * 32 + g * 8]));
 #pragma unroll
-            for (int ns = 0; ns < 4; ns++) {
-                const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bs[buf][part][ns * 16 + r][g * 8]));
+            for (int ms = 0; ms < 4; ms++) {
+                const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4 *>(&As[buf][wt * 64 + ms * 16 + r][kk * 32 + g * 8]));
 #pragma unroll
-                for (int ms = 0; ms < 2; ms++) acc[ms][ns] = mfma16x16x32(af[ms], bfr, acc[ms][ns]);
+                for (int part = 0; part < 3; part++) acc[ms] = mfma16x16x32(af, bfr[part], acc[ms]);
             }
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
+    };
+    // Iteration kt: stage kt in LDS buffer kt % 2, stage kt + 1 in flight in registers
+    // (issued two iterations ago), stage kt + 2 issued now into the registers freed by the
+    // previous iteration's store.
+    const int nk = H / RBK;  // >= 4
+    RouterStage s0, s1;
+    gload(0, s0);
+    gload(RBK, s1);
+    lstore(0, s0);
+    __syncthreads();
+    auto step = [&](int kt, RouterStage &nxt, RouterStage &fill) {
+        if (kt + 2 < nk) gload((kt + 2) * RBK, fill);
+        compute(kt & 1);
+        if (kt + 1 < nk) lstore((kt + 1) & 1, nxt);
         __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, s1, s0);      // stage kt + 1 sits in s1; s0 (stored) takes stage kt + 2
+        step(kt + 1, s0, s1);  // stage kt + 2 sits in s0; s1 takes stage kt + 3
     }
-    // acc[ms][ns][i] = logit of token t0 + wave*32 + ms*16 + 4g + i, expert e0 + ns*16 + r
+    // acc[ms][i] = logit of token t0 + wt*64 + ms*16 + 4g + i, expert e0 + we*16 + r
+    const int e = e0 + we * 16 + r;
+    const float bv = (bias && e < E) ? bias[e] : 0.f;
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++)
+    for (int ms = 0; ms < 4; ms++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int t = t0 + wave * 32 + ms * 16 + 4 * g + i;
-            if (t >= T) continue;
-#pragma unroll
-            for (int ns = 0; ns < 4; ns++) {
-                const int e = e0 + ns * 16 + r;
-                if (e < E) logits[(size_t)t * E + e] = acc[ms][ns][i] + (bias ? bias[e] : 0.f);
-            }
+            const int t = t0 + wt * 64 + ms * 16 + 4 * g + i;
+            if (t < T && e < E) logits[(size_t)t * E + e] = acc[ms][i] + bv;
         }
 }
 
@@ -149,7 +164,7 @@ hipError_t launch_router(const Shape &s, int64_t T, const uint16_t *x, const flo
         router_small_kernel<32><<<s.E, 256, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
     } else {
         dim3 grid((unsigned)((T + RBM - 1) / RBM), (unsigned)((s.E + RBN - 1) / RBN));
-        router_mfma_kernel<<<grid, 256, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
+        router_mfma_kernel<<<grid, RNT, 0, st>>>((int)T, s.H, s.E, x, Wr, bias, logits);
     }
     return hipGetLastError();
 }
