@@ -16,13 +16,13 @@
 //            of every selected expert: the single token is the same for every expert) and
 //            its share of the expert's down rows of the H-slice, copied HBM -> LDS without
 //            registers.  The later selection rounds run while the first slots stream.
-//   wait     for the (k + 1) * I words of h.
+//   wait     for the words of h: one per (pair of slots, row of I), two bf16 values each.
 //   phase 3  down rows from LDS against h (bf16, as on every path), one slot per wave and
 //            8 lanes per row; combine (shared first, then j ascending) -> y.
 //
-// Cross-workgroup data (logits, h) moves as 64-bit exchange words {launch tag, fp32 value}
+// Cross-workgroup data (logits, h) moves as 64-bit exchange words {launch tag, payload}
 // written with agent-scope stores and polled with agent-scope loads: one aligned 64-bit
-// access carries the value and its readiness together, so there are no grid barriers,
+// access carries the payload and its readiness together, so there are no grid barriers,
 // fences or cache-wide write-backs, and a reader waits one round trip after the word it
 // needs lands.  The tag is the launch counter at the start of the workspace plus one;
 // workgroup 0 advances the counter once it has seen every workgroup's phase-1 word (each
@@ -44,7 +44,10 @@ constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
 
 // Workspace words of this launch (the zero-initialised head of the workspace):
 // u32 [0] launch counter, u32 [1] error flag; u64 exchange words for the logits at byte
-// 1024 (one per workgroup) and for h at byte 3072 ([k + 1][I], slot k = shared expert).
+// 1024 (one per workgroup: the fp32 logit) and for h at byte 3072 ([(k + S + 1) / 2][I]:
+// word (q, i) holds bf16 h of slots 2 q (low half) and 2 q + 1 (high half) at row i; slot
+// k = shared expert).  Every workgroup reads all of h, so two values per word halve the
+// polling traffic, and h is rounded to bf16 before the down rows on every path anyway.
 // A chain of layers hands each token to the next launch through the bf16 [2048] buffer at
 // kXNextOff.
 constexpr int kCtlEpoch = 0, kCtlError = 1;
@@ -65,6 +68,12 @@ __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds)
 __device__ __forceinline__ void put_word(uint64_t *p, uint32_t tag, float v)
 {
     __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// h of two slots at one row of I: bf16(lo) in bits 0-15, bf16(hi) in bits 16-31.
+__device__ __forceinline__ void put_h2(uint64_t *p, uint32_t tag, float lo, float hi)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | f2bf(lo) | (f2bf(hi) << 16), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t get_word(const uint64_t *p)
 {
@@ -187,7 +196,8 @@ struct D1Args {
     int32_t *counts, *offsets, *sa, *ap;  // null in a chain
     uint32_t *ctl;   // launch counter, error flag
     uint64_t *xlog;  // [256] exchange words: logit of expert b (workgroup b)
-    uint64_t *xh;    // [k + S][I] exchange words: slot j < k = j-th selected expert, slot k = shared
+    uint64_t *xh;    // [(k + S + 1) / 2][I] exchange words, two slots each: slot j < k = j-th
+                     // selected expert, slot k = shared
 };
 
 __device__ __forceinline__ const uint8_t *mat_base(const WMat &m, int e, int E, size_t bytes)
@@ -359,7 +369,10 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         }
     }
     __syncthreads();
-    if (S && tid < npair) put_word(a.xh + (size_t)k * I + i0 + tid, tag, silu(sh.gs[tid]) * sh.us[tid]);
+    // the shared slot k has a word of its own when k is even; otherwise it shares one with
+    // slot k - 1 and goes out in phase 2
+    if (S && (k & 1) == 0 && tid < npair)
+        put_h2(a.xh + (size_t)(k / 2) * I + i0 + tid, tag, silu(sh.gs[tid]) * sh.us[tid], 0.f);
 
     // ---------------- phase 2: selection (every wave), routed gate/up rows, down rows
     if (wave == 0) {
@@ -442,9 +455,12 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     }
     if (FMT == 1 && wave == 0 && lane < ns) sh.dts[lane] = dts;
     __syncthreads();  // also completes this workgroup's HBM -> LDS copies
-    for (int q = tid; q < k * npair; q += 512) {
-        const int j = q / npair, p = q - j * npair;
-        put_word(a.xh + (size_t)j * I + i0 + p, tag, silu(sh.g[j][p]) * sh.u[j][p]);
+    for (int q = tid; q < (k + 1) / 2 * npair; q += 512) {
+        const int jp = q / npair, p = q - jp * npair, j = 2 * jp;
+        const float lo = silu(sh.g[j][p]) * sh.u[j][p];
+        const float hi = j + 1 < k ? silu(sh.g[j + 1][p]) * sh.u[j + 1][p]
+                                   : (S ? silu(sh.gs[p]) * sh.us[p] : 0.f);  // slot k: shared
+        put_h2(a.xh + (size_t)jp * I + i0 + p, tag, lo, hi);
     }
     if (b == 0 && tid < 64) {  // publish the routing tensors (the single token: t = 0)
         if (tid < k) {
@@ -472,15 +488,20 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 
     // ---------------- phase 3: down rows from LDS against h, combine
     {
-        constexpr int NH = (kMaxK + 1) * 1024 / 512;
-        const int nh = ns * I, nq = tid < nh ? (nh - tid + 511) / 512 : 0;
+        constexpr int NH = (kMaxK + 2) / 2 * 1024 / 512;
+        const int nh = (ns + 1) / 2 * I, nq = tid < nh ? (nh - tid + 511) / 512 : 0;
         uint64_t hw[NH];
 #pragma unroll
         for (int q = 0; q < NH; q++) hw[q] = q < nq ? get_word(a.xh + tid + 512 * q) : 0ull;
         await_words<NH>(a.xh + tid, 512, nq, hw, tag, a.ctl);
 #pragma unroll
-        for (int q = 0; q < NH; q++)
-            if (q < nq) sh.hb[tid + 512 * q] = f2bf(__uint_as_float((uint32_t)hw[q]));
+        for (int q = 0; q < NH; q++) {
+            if (q < nq) {
+                const int wdx = tid + 512 * q, jp = wdx / I, i = wdx - jp * I;
+                sh.hb[(size_t)(2 * jp) * I + i] = (uint16_t)(hw[q] & 0xffffu);
+                if (2 * jp + 1 < ns) sh.hb[(size_t)(2 * jp + 1) * I + i] = (uint16_t)((hw[q] >> 16) & 0xffffu);
+            }
+        }
     }
     __syncthreads();
     // Wave w takes slot j = w (and j + 8); lane = (row n = lane / 8, part s = lane % 8):
