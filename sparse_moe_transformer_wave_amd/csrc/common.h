@@ -311,11 +311,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 // +0, NaN below -inf), low word = 0xffff - e so that equal logits prefer the lower index.
 __device__ __forceinline__ uint64_t select_key(float v, int e)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t ord;
-    if ((u & 0x7fffffffu) > 0x7f800000u) ord = 0u;           // NaN: below everything
-    else if (u == 0x80000000u) ord = 0x80000000u;              // -0 == +0
-    else ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(v);
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    ord = u == 0x80000000u ? 0x80000000u : ord;               // -0 == +0
+    ord = (u & 0x7fffffffu) > 0x7f800000u ? 0u : ord;         // NaN: below everything
     return ((uint64_t)ord << 32) | (uint64_t)(0xffffu - (uint32_t)e);
 }
 
@@ -352,11 +351,14 @@ __device__ __forceinline__ void topk_4tokens(const float *__restrict__ lg, int l
     const int lane = threadIdx.x & 63, g = lane >> 4, L = lane & 15, t = t0 + g;
     const bool live = t < T;
     const float *lt = lg + (size_t)(live ? t : t0) * ldl;
+    float lv[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) lv[i] = lt[L + 16 * i < E ? L + 16 * i : 0];  // all reads in flight together
     uint32_t key[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const int e = L + 16 * i;
-        key[i] = (live && e < E) ? (uint32_t)(select_key(lt[e], e) >> 32) + 1u : 0u;
+        key[i] = (live && e < E) ? (uint32_t)(select_key(lv[i], e) >> 32) + 1u : 0u;
     }
     int sel[8];
 #pragma unroll
@@ -387,6 +389,51 @@ __device__ __forceinline__ void topk_4tokens(const float *__restrict__ lg, int l
             ids[(size_t)t * k + j] = sel[j];
             wout[(size_t)t * k + j] = renorm ? sg[j] / sum : sg[j];
         }
+    }
+}
+
+// One token per wave (the small-batch launch, where the selecting workgroup has more waves
+// than tokens): lane l holds experts l + 64 i (i < 4) as the same 32-bit keys.  Each round
+// takes the wave maximum; among equal keys the lowest expert wins: the first i with a match
+// in any lane (one ballot per i), and in it the lowest lane.  Lane j < k then writes
+// ids[j] and the j-th sigmoid weight (renormalised over the k selected, summed in j order).
+// lt: the token's E logits.
+__device__ __forceinline__ void topk_wave(const float *__restrict__ lt, int E, int k, int renorm,
+                                          int32_t *__restrict__ ids, float *__restrict__ wout)
+{
+    const int lane = threadIdx.x & 63;
+    float lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) lv[i] = lt[lane + 64 * i < E ? lane + 64 * i : 0];
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? (uint32_t)(select_key(lv[i], e) >> 32) + 1u : 0u;
+    }
+    int mine = 0;  // lane j < k: the j-th selected expert
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        if (j >= k) break;
+        const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+        const uint64_t b0 = __ballot(key[0] == m), b1 = __ballot(key[1] == m);
+        const uint64_t b2 = __ballot(key[2] == m), b3 = __ballot(key[3] == m);
+        const int i = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
+        const int wl = __builtin_ctzll(b0 ? b0 : b1 ? b1 : b2 ? b2 : b3);
+        if (lane == wl) {
+            key[0] = i == 0 ? 0u : key[0];
+            key[1] = i == 1 ? 0u : key[1];
+            key[2] = i == 2 ? 0u : key[2];
+            key[3] = i == 3 ? 0u : key[3];
+        }
+        if (lane == j) mine = wl + 64 * i;
+    }
+    const float sg = 1.0f / (1.0f + expf(-lt[lane < k ? mine : 0]));
+    float sum = 0.f;
+    for (int j = 0; j < k; j++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), j));
+    if (lane < k) {
+        ids[lane] = mine;
+        wout[lane] = renorm ? sg / sum : sg;
     }
 }
 

@@ -169,18 +169,31 @@ __global__ __launch_bounds__(1024) void permute_kernel(int T, int E, int k, int 
 // one work item each (no expert holds more than kGemvMaxT * 8 rows).
 struct SmallGroup {
     int cnt[257], off[258], flag[257], idx[258];
+    int wcnt[4][256];  // per wave of assignments: how many of them went to each expert
 };
 
 __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_ids, SmallGroup &g,
                                  int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                  int32_t *__restrict__ sa, int32_t *__restrict__ ap, const Plan &p)
 {
-    const int tid = threadIdx.x, n = T * k;
+    const int tid = threadIdx.x, n = T * k, lane = tid & 63, wv = tid >> 6;
     if (tid < E) g.cnt[tid] = 0;
+    (&g.wcnt[0][0])[tid] = 0;  // 1024 entries, one per thread
     __syncthreads();
     const int e = tid < n ? s_ids[tid] : -1;
     const bool valid = e >= 0 && e < E;
     if (valid) atomicAdd(&g.cnt[e], 1);
+    // lanes of this wave with the same expert (one ballot per id bit) and the rank among them
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t vote = __ballot(bit);
+        peers &= bit ? vote : ~vote;
+    }
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) g.wcnt[wv][e] = __popcll(peers);
     __syncthreads();
     if (tid < 64) wave0_exclusive_scan(g.cnt, g.off, E);
     __syncthreads();
@@ -189,9 +202,9 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
         offsets[tid] = g.off[tid];
     }
     if (tid == 0) offsets[E] = g.off[E];
-    if (valid) {
-        int before = 0;
-        for (int a = 0; a < tid; a++) before += s_ids[a] == e;
+    if (valid) {  // stable: earlier waves' assignments of e, then this wave's lower lanes
+        int before = rank;
+        for (int w = 0; w < wv; w++) before += g.wcnt[w][e];
         const int pos = g.off[e] + before;
         sa[pos] = tid;
         ap[tid] = pos;
@@ -225,9 +238,10 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
 // wave w takes tokens w and w + 16) computes the logits of expert e and writes them with
 // agent-scope write-through stores; once they have completed it counts itself in at an
 // agent-scope arrival counter.  The workgroup that arrives last has every logit: it reads
-// them back with agent-scope loads into LDS, selects the top-k of every token (four
-// tokens per wave), groups the assignments by expert and writes the plan, so the expert
-// kernels that follow need no routing step of their own.  It also re-arms the counter.
+// them back with agent-scope loads into LDS, selects the top-k of every token (one token
+// per wave; four per wave measured slower at 32 tokens), groups the assignments by expert
+// and writes the plan, so the expert kernels that follow need no routing step of their own.
+// It also re-arms the counter.
 __global__ __launch_bounds__(1024) void router_select_kernel(
     int T, int H, int E, int k, int S, int renorm, const uint16_t *__restrict__ x,
     const float *__restrict__ Wr, const float *__restrict__ bias, float *__restrict__ logits,
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(1024) void router_select_kernel(
         s_lg[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(arrivals, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (4 * wv < T) topk_4tokens(s_lg, E, 4 * wv, T, E, k, renorm, s_ids, s_w);  // 4 tokens per wave
+    for (int t = wv; t < T; t += 16) topk_wave(s_lg + (size_t)t * E, E, k, renorm, s_ids + t * k, s_w + t * k);
     __syncthreads();
     for (int a = tid; a < T * k; a += 1024) {
         ids[a] = s_ids[a];
