@@ -303,8 +303,10 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
     if (ws_bytes < L.total) return FLINT_ERR_WORKSPACE;
     const Plan plan = plan_view(ws, L, s);
     hipStream_t st = (hipStream_t)stream;
-    rc = hip_status(launch_plan(s, T, dense ? nullptr : offsets, plan, st));
-    if (rc) return rc;
+    if (!dense || T > kGemvMaxT) {  // the streaming kernels take a dense layer's plan as implicit
+        rc = hip_status(launch_plan(s, T, dense ? nullptr : offsets, plan, st));
+        if (rc) return rc;
+    }
     return forward_impl(s, wset_of(weights), T, x, topk_w, sorted_assign, assign_pos, y, ws, L,
                         plan, st);
 }
@@ -345,8 +347,10 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     hipStream_t st = (hipStream_t)stream;
     const Plan plan = plan_view(ws, L, s);
     if (dense) {
-        rc = hip_status(launch_plan(s, T, nullptr, plan, st));
-        if (rc) return rc;
+        if (T > kGemvMaxT) {  // the streaming kernels take a dense layer's plan as implicit
+            rc = hip_status(launch_plan(s, T, nullptr, plan, st));
+            if (rc) return rc;
+        }
         return forward_impl(s, wset_of(weights), T, x, nullptr, nullptr, nullptr, y, ws, L, plan, st);
     }
     if (T == 1 && decode1_supported(s, weights->format)) {

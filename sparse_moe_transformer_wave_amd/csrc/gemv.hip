@@ -44,7 +44,7 @@ __device__ __forceinline__ float expert_ts(const WMat &m, int e, int E)
 // launch to units with at most 16 tokens (1) or more (2); 0 takes every unit.
 template <int FMT, int NMT, int RG>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, int E, int k, int cls,
-                                                          WSet w, const uint16_t *__restrict__ x,
+                                                          int dense, WSet w, const uint16_t *__restrict__ x,
                                                           const int32_t *__restrict__ sa_in,
                                                           Plan p, uint16_t *__restrict__ h)
 {
@@ -54,8 +54,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     // The unit's plan entry loads together with the unit count (one round trip), then the
     // token indices of the A rows together with the first weights (one more).
-    const int nT = p.meta[0];
-    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    // a dense layer's plan is implicit: one unit, the T tokens in slots 0 .. T - 1
+    const int nT = dense ? 1 : p.meta[0];
+    const int e = dense ? E : p.touched[u], base = dense ? 0 : p.tbase[u], cnt = dense ? T : p.tcount[u];
     if (u >= nT || (cls == 1 && cnt > 16) || (cls == 2 && cnt <= 16)) return;
     int tix[NMT];
 #pragma unroll
@@ -238,17 +239,18 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 // workspace in fp32.  `cls` as for gate/up.  Thousands of small independent workgroups
 // keep the weight stream busy the way the gate/up pass does.
 template <int FMT, int NMT, int KS>
-__global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int cls, WSet w,
+__global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int cls, int dense_T, WSet w,
                                                         const uint16_t *__restrict__ h, Plan p,
-                                                        float *__restrict__ o)
+                                                        float *__restrict__ o, uint16_t *__restrict__ y)
 {
     static_assert(KS == 1 || KS == 4, "K split over the 4 waves or none");
     __shared__ f32x4 red[KS == 4 ? 3 : 1][NMT][64];
     const int nrb = H / (64 / KS);
     const int u = blockIdx.x / nrb, nb = blockIdx.x - u * nrb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    const int nT = p.meta[0];
-    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    // dense_T > 0: a dense layer, one implicit unit of dense_T tokens whose outputs are y
+    const int nT = dense_T ? 1 : p.meta[0];
+    const int e = dense_T ? E : p.touched[u], base = dense_T ? 0 : p.tbase[u], cnt = dense_T ? dense_T : p.tcount[u];
     if (u >= nT || (cls == 1 && cnt > 16) || (cls == 2 && cnt <= 16)) return;
     const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * 16 + r;  // MFMA column r of this wave
     const int kw = KS == 1 ? 0 : wave;  // this wave's part of K
@@ -373,7 +375,12 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int ti = mt * 16 + 4 * g + i;
-            if ((NMT == 1 || mt < nmt) && ti < cnt) o[(size_t)(base + ti) * H + row] = acc[mt][i] * ts;
+            if ((NMT == 1 || mt < nmt) && ti < cnt) {
+                if (dense_T)  // the combine of a dense layer is y = bf16(o): written here
+                    y[(size_t)ti * H + row] = (uint16_t)f2bf(acc[mt][i] * ts);
+                else
+                    o[(size_t)(base + ti) * H + row] = acc[mt][i] * ts;
+            }
         }
 }
 
@@ -437,24 +444,29 @@ static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, in
 {
     constexpr int RG = FMT != 1 && NMT == 1 ? 2 : 1;
     const unsigned grid = (unsigned)(maxU * (s.I / (8 * RG)));
-    gemv_gateup_kernel<FMT, NMT, RG><<<grid, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, w, x, sa, plan, h);
+    gemv_gateup_kernel<FMT, NMT, RG><<<grid, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, s.E == 0, w, x, sa,
+                                                         plan, h);
 }
 
 // Split K over the waves when 64-row workgroups would leave most CUs idle.
 template <int FMT, int NMT>
-static void launch_down(const Shape &s, const WSet &w, int maxU, int cls, const uint16_t *h,
-                        const Plan &plan, float *o, hipStream_t st)
+static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, int cls, const uint16_t *h,
+                        const Plan &plan, float *o, uint16_t *y, hipStream_t st)
 {
+    const int dense_T = s.E == 0 ? (int)T : 0;
     if (maxU * (s.H / 64) >= 512)
-        gemv_down_kernel<FMT, NMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, cls, w, h, plan, o);
+        gemv_down_kernel<FMT, NMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, cls, dense_T, w, h,
+                                                                                  plan, o, y);
     else
-        gemv_down_kernel<FMT, NMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, cls, w, h, plan, o);
+        gemv_down_kernel<FMT, NMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, cls, dense_T, w, h,
+                                                                                  plan, o, y);
 }
 
 // With routed experts the plan lists units of at most 16 tokens (an expert with more is
 // split; in practice the shared expert once T > 16), so one launch of the one-tile
 // kernels covers every unit.  A dense layer (E = 0) keeps its single unit whole, so its
-// weights are read once: the two-tile kernels for T > 16.
+// weights are read once: the two-tile kernels for T > 16.  Its plan is implicit (no plan
+// launch) and its down pass writes y (no combine launch).
 template <int FMT>
 static void launch_stream(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                           const float *topk_w, const int32_t *sa, const int32_t *ap,
@@ -464,11 +476,12 @@ static void launch_stream(const Shape &s, const WSet &w, int64_t T, const uint16
                            (int64_t)s.S * ((T + kUnitRows - 1) / kUnitRows));
     if (s.E > 0 || T <= 16) {
         launch_gateup<FMT, 1>(s, w, T, maxU, 0, x, sa, plan, h, st);
-        launch_down<FMT, 1>(s, w, maxU, 0, h, plan, o, st);
+        launch_down<FMT, 1>(s, w, T, maxU, 0, h, plan, o, y, st);
     } else {
         launch_gateup<FMT, 2>(s, w, T, 1, 0, x, sa, plan, h, st);
-        launch_down<FMT, 2>(s, w, 1, 0, h, plan, o, st);
+        launch_down<FMT, 2>(s, w, T, 1, 0, h, plan, o, y, st);
     }
+    if (s.E == 0) return;
     const int nthreads = (int)T * (s.H / 8);
     gemv_combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o, topk_w, ap, y);
 }
