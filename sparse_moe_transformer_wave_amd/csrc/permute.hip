@@ -325,13 +325,19 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int T, int E, int k, int
     __shared__ int cnt[256];
     __shared__ int off[257];
     __shared__ PlanScratch ps;
+    // Thread e: expert e's count over the blocks, then (once the offsets are known) its
+    // base in every block = offset of e + the counts of e in earlier blocks.  The block
+    // counts are read 16 at a time, every read of a batch in flight together.
+    constexpr int B = 16;
     const int e = threadIdx.x;
     int tot = 0;
     if (e < E)
-        for (int b = 0; b < nb; b++) {
-            const int c = hist[(size_t)b * E + e];
-            hist[(size_t)b * E + e] = tot;  // exclusive prefix over blocks
-            tot += c;
+        for (int b0 = 0; b0 < nb; b0 += B) {
+            int c[B];
+#pragma unroll
+            for (int i = 0; i < B; i++) c[i] = b0 + i < nb ? hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < B; i++) tot += c[i];
         }
     if (e < 256) cnt[e] = (e < E) ? tot : 0;
     __syncthreads();
@@ -340,7 +346,17 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int T, int E, int k, int
     if (e < E) {
         counts[e] = cnt[e];
         offsets[e] = off[e];
-        for (int b = 0; b < nb; b++) hist[(size_t)b * E + e] += off[e];
+        int run = off[e];
+        for (int b0 = 0; b0 < nb; b0 += B) {
+            int c[B];
+#pragma unroll
+            for (int i = 0; i < B; i++) c[i] = b0 + i < nb ? hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < B; i++) {
+                if (b0 + i < nb) hist[(size_t)(b0 + i) * E + e] = run;
+                run += c[i];
+            }
+        }
     }
     if (e == 0) offsets[E] = off[E];
     if (with_plan) build_plan(T, E, k, S, H, cnt, off, plan, ps);
