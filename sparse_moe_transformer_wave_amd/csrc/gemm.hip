@@ -335,6 +335,205 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
     }
 }
 
+// ---------------------------------------------------------------- NVFP4 / INT4: codes to LDS once
+// The same 256 x 256 tiles as gemm_bf16_kernel, here with 8 waves (two per SIMD) of
+// 64 slots x 128 B rows each, so the registers hold what the 4-bit path adds.  The tokens
+// (A) come through a 5-stage ring of 32-wide K stages filled HBM -> LDS by
+// global_load_lds_dwordx4, four stages ahead.  The weights arrive as their 4-bit codes:
+// per stage a thread loads 16 codes of one row (8 bytes) and their scale into a 4-slot
+// register ring, four stages ahead as well, so the weight bytes in flight are a quarter of
+// bf16's; when the stage comes up it turns them into 16 exact bf16 values (NVFP4: e2m1
+// times the E4M3 block scale; INT4: q times the bf16 group scale, rounded once, as in
+// grouped_gemm_kernel's staging) and writes them to a double-buffered bf16 B stage in the
+// ring's swizzled layout, where every wave reads its fragments.  Copies and loads go out
+// per stage s as A(s) (two per wave), codes(s), scale(s), so with stage s + 4 issued in
+// iteration s, stage s has landed once at most twelve are in flight.  The loop runs four
+// stages per trip (the register slots stay fixed) and its steady state has no branches.
+constexpr int NTQ = 512;
+template <int MODE, int FMT>
+__global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E, int k, WSet w,
+                                                      const uint16_t *__restrict__ asrc,
+                                                      const int32_t *__restrict__ sa, Plan p,
+                                                      uint16_t *__restrict__ out)
+{
+    constexpr int kRow = 64, kStage = 256 * kRow;  // bytes: one A stage, one B stage
+    constexpr int NSA = 5;                         // A ring stages
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // NSA A stages + 2 B stages
+    uint8_t *const bbuf = lds + NSA * kStage;
+    const int N = MODE == 0 ? 2 * I : H;
+    const int n_tiles = N / BN;
+    int item, nb;
+    xcd_map(blockIdx.x, n_tiles, item, nb);
+    if (item >= p.meta[1]) return;
+    const int code = p.items[item];
+    const int u = code >> 16, mtile = code & 0xffff;
+    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    const bool sh = (e == E);
+    const int m0 = mtile * BM;
+    const int valid = min(BM, cnt - m0);
+    const int K = MODE == 0 ? H : I;
+    const int nk = K / 32;  // a multiple of 4
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // A copies: wave w fills rows 32 w + 16 c + l / 4 (c < 2) of every stage, slot l % 4,
+    // i.e. logical chunk (l % 4) ^ ((row >> 2) & 3).  Rows past the tile repeat the last.
+    const uint16_t *ap_[2];
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+        const int crow = 32 * wave + 16 * c + (lane >> 2);
+        const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);
+        const int ri = min(crow, valid - 1);
+        if (MODE == 0) {
+            const int tok = sh ? base - T * k + m0 + ri : sa[base + m0 + ri] / k;
+            ap_[c] = asrc + (size_t)tok * H + 8 * cchunk;
+        } else {
+            ap_[c] = asrc + (size_t)(base + m0 + ri) * I + 8 * cchunk;
+        }
+    }
+    uint8_t *const cdst = lds + 2048 * wave;  // + slot * kStage
+    auto issue_a = [&](int kt, int slot) {
+        lds_copy16(ap_[0] + 32 * kt, cdst + slot * kStage);
+        lds_copy16(ap_[1] + 32 * kt, cdst + slot * kStage + 1024);
+    };
+
+    // Codes: thread tid takes B row bro = tid / 2 of the tile and k 16 hq .. 16 hq + 15 of
+    // every stage (hq = tid % 2): logical chunks 2 hq and 2 hq + 1 of row bro.  Gate/up:
+    // each 128-row wave column holds 64 gate rows, then the same 64 up rows.
+    const int bro = tid >> 1, hq = tid & 1;
+    const uint8_t *qp;
+    const uint8_t *sp;
+    {
+        const WMat *mat;
+        int n;
+        if (MODE == 0) {
+            const int wcol = bro >> 7, within = bro & 127;
+            mat = (within >> 6) ? &w.up : &w.gate;
+            n = nb * (BN / 2) + wcol * 64 + (within & 63);
+        } else {
+            mat = &w.down;
+            n = nb * BN + bro;
+        }
+        const size_t mb = (size_t)H * I / 2, srow = scale_row_bytes(FMT, K), sb = (size_t)(H * I / K) * srow;
+        qp = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2) + 8 * hq;
+        // NVFP4: block 2 s + hq of the row (16 codes); INT4: group s / 4 (bf16)
+        sp = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * srow + (FMT == 1 ? hq : 0);
+    }
+    u32x2 cq[4];
+    uint32_t cs[4];
+    auto issue_b = [&](int kt, int slot) {
+        cq[slot] = *reinterpret_cast<const u32x2 *>(qp + 16 * kt);
+        cs[slot] = FMT == 1 ? (uint32_t)sp[2 * kt] : (uint32_t)reinterpret_cast<const uint16_t *>(sp)[kt >> 2];
+    };
+    auto dequant_b = [&](int kt, int slot) {  // stage kt's codes -> bf16 B buffer kt % 2
+        const float sc = FMT == 1 ? e4m3_to_f32(cs[slot]) : bf2f(cs[slot]);
+        uint8_t *row = bbuf + (kt & 1) * kStage + bro * kRow;
+        const int sw = (bro >> 2) & 3;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+            const uint32_t qw = cq[slot][h2];
+            const u32x4 v = FMT == 1 ? dequant8(qw, sc) : dequant8_int4(qw, sc);
+            *reinterpret_cast<u32x4 *>(row + 16 * ((2 * hq + h2) ^ sw)) = v;
+        }
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment reads: A row wm*64 + 16 ms + r and B row wn*128 + 16 ns + r, logical chunk g.
+    const int fslot = 16 * (g ^ ((r >> 2) & 3));
+    const int aoff = (wm * 64 + r) * kRow + fslot, boff = (wn * 128 + r) * kRow + fslot;
+    auto compute = [&](int kt) {
+        const uint8_t *as = lds + (kt % NSA) * kStage + aoff;
+        const uint8_t *bs = bbuf + (kt & 1) * kStage + boff;
+        bf16x8 af[4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ms++) af[ms] = as_bf16x8(*reinterpret_cast<const u32x4 *>(as + ms * 16 * kRow));
+#pragma unroll
+        for (int ns = 0; ns < 8; ns++) {
+            const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const u32x4 *>(bs + ns * 16 * kRow));
+#pragma unroll
+            for (int ms = 0; ms < 4; ms++) acc[ms][ns] = mfma16x16x32(af[ms], bfr, acc[ms][ns]);
+        }
+    };
+    // Iteration kt: stage kt landed (A in its ring slot, codes in register slot kt % 4);
+    // its codes become bf16 in B buffer kt % 2 (last read in iteration kt - 2, before the
+    // previous barrier); the barrier makes A and B of stage kt visible and frees A slot
+    // (kt + 4) % 5 (read in kt - 1), which stage kt + 4 refills together with the codes
+    // slot just used; then the MFMAs.
+    auto step = [&](int kt, int cslot, bool more) {
+        dequant_b(kt, cslot);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (more) {
+            issue_a(kt + 4, (kt + 4) % NSA);
+            issue_b(kt + 4, cslot);
+        }
+        compute(kt);
+    };
+
+#pragma unroll
+    for (int s0 = 0; s0 < 4; s0++) {
+        issue_a(s0, s0);
+        issue_b(s0, s0);
+    }
+    int kt = 0;
+    for (; kt + 8 <= nk; kt += 4) {  // every stage of this trip issues stage + 4
+        wait_vmcnt<12>();
+        step(kt, 0, true);
+        wait_vmcnt<12>();
+        step(kt + 1, 1, true);
+        wait_vmcnt<12>();
+        step(kt + 2, 2, true);
+        wait_vmcnt<12>();
+        step(kt + 3, 3, true);
+    }
+    // last four stages: nothing more to issue, so fewer copies are in flight at each wait
+    wait_vmcnt<12>();
+    step(kt, 0, false);
+    wait_vmcnt<8>();
+    step(kt + 1, 1, false);
+    wait_vmcnt<4>();
+    step(kt + 2, 2, false);
+    wait_vmcnt<0>();
+    step(kt + 3, 3, false);
+
+    // Epilogue.  acc[ms][ns][i] = D[row = wm*64 + ms*16 + 4g + i][brow = wn*128 + ns*16 + r].
+    float tsg = 1.f, tsu = 1.f, tsd = 1.f;  // NVFP4 tensor scales
+    if (FMT == 1) {
+        tsg = sh ? *w.gate.ts_shared : w.gate.ts_routed[e];
+        tsu = sh ? *w.up.ts_shared : w.up.ts_routed[e];
+        tsd = sh ? *w.down.ts_shared : w.down.ts_routed[e];
+    }
+#pragma unroll
+    for (int ms = 0; ms < 4; ms++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = wm * 64 + ms * 16 + 4 * g + i;
+            if (row >= valid) continue;
+            const size_t slot = (size_t)(base + m0 + row);
+            if (MODE == 0) {
+#pragma unroll
+                for (int ns = 0; ns < 4; ns++) {
+                    const int col = nb * (BN / 2) + wn * 64 + ns * 16 + r;
+                    const float gv = acc[ms][ns][i] * tsg, uv = acc[ms][ns + 4][i] * tsu;
+                    out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
+                }
+            } else {
+#pragma unroll
+                for (int ns = 0; ns < 8; ns++) {
+                    const int col = nb * BN + wn * 128 + ns * 16 + r;
+                    out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i] * tsd);
+                }
+            }
+        }
+    }
+}
+
 // y[t][n] = bf16(o[T*k + t][n] + sum_j w[t][j] * o[ap[t*k + j]][n]); 8 columns per thread.
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int S,
                                                       const uint16_t *__restrict__ o,
@@ -389,12 +588,21 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
         constexpr size_t lds = (size_t)kRingStages * 2 * 256 * 64;
         gemm_bf16_kernel<0, kRingStages><<<g1, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
-    } else if (w.fmt == 1) {
-        grouped_gemm_kernel<0, 1><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        grouped_gemm_kernel<1, 1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     } else {
-        grouped_gemm_kernel<0, 2><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        grouped_gemm_kernel<1, 2><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        // 4-bit weights: the code ring needs K in whole trips of four 32-wide stages
+        constexpr size_t qlds = (size_t)(5 + 2) * 256 * 64;
+        const bool ring_gu = s.H % 128 == 0, ring_dn = s.I % 128 == 0;
+        if (w.fmt == 1) {
+            if (ring_gu) gemm_q4_kernel<0, 1><<<g1, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+            else grouped_gemm_kernel<0, 1><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+            if (ring_dn) gemm_q4_kernel<1, 1><<<g2, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+            else grouped_gemm_kernel<1, 1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        } else {
+            if (ring_gu) gemm_q4_kernel<0, 2><<<g1, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+            else grouped_gemm_kernel<0, 2><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+            if (ring_dn) gemm_q4_kernel<1, 2><<<g2, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+            else grouped_gemm_kernel<1, 2><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        }
     }
     const int64_t nthreads = T * (s.H / 8);
     combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o,
