@@ -323,19 +323,29 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     };
 
     // ---------------- phase 1
-    if (S) load_down(k, E);
-    if (wave == 0) {
-        const int e = b;  // E <= 256: workgroup b computes logit b, if there is one
-        if (e < E) {      // router row: one logit, all loads in flight
-            const float4 *w4 = reinterpret_cast<const float4 *>(a.Wr + (size_t)e * H);
-            float4 wv[8];
-            u32x2 xv[8];
+    // bf16: the router row goes out first: every workgroup's other copies wait for the
+    // barrier below, so the 2 MB of router rows are ahead of the shared expert's 9 MB in the
+    // memory queues and the logits, on which everything after depends, come back sooner
+    // (with 4-bit weights the shared expert is 2.6 MB and holding it back measured slower).
+    if (FMT != 0 && S) load_down(k, E);
+    float4 wv[8];
+    u32x2 xv[8];
+    if (wave == 0 && b < E) {  // E <= 256: workgroup b computes logit b, if there is one
+        const float4 *w4 = reinterpret_cast<const float4 *>(a.Wr + (size_t)b * H);
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int c = lane + 64 * i;
-                wv[i] = c < H / 4 ? w4[c] : float4{0.f, 0.f, 0.f, 0.f};
-                xv[i] = c < H / 4 ? *reinterpret_cast<const u32x2 *>(a.x + 4 * c) : u32x2{0u, 0u};
-            }
+        for (int i = 0; i < 8; i++) {
+            const int c = lane + 64 * i;
+            wv[i] = c < H / 4 ? w4[c] : float4{0.f, 0.f, 0.f, 0.f};
+            xv[i] = c < H / 4 ? *reinterpret_cast<const u32x2 *>(a.x + 4 * c) : u32x2{0u, 0u};
+        }
+    }
+    if (FMT == 0) {
+        __syncthreads();
+        if (S) load_down(k, E);
+    }
+    if (wave == 0) {
+        const int e = b;
+        if (e < E) {      // router row: one logit
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
