@@ -11,12 +11,15 @@
 //            shared expert's down rows of this workgroup's H-slice go straight into LDS.
 //   wait     for the 256 logit words.
 //   phase 2  every wave selects the top-k of the 256 logits itself (same code, same bits,
-//            so every copy agrees).  Right after round j it issues its loads for slot j:
-//            its gate/up row of that expert (workgroup b owns rows [b I/256, (b+1) I/256)
-//            of every selected expert: the single token is the same for every expert) and
-//            its share of the expert's down rows of the H-slice, copied HBM -> LDS without
-//            registers.  The later selection rounds run while the first slots stream.
-//   wait     for the words of h: one per (pair of slots, row of I), two bf16 values each.
+//            so every copy agrees).  Right after round j it issues its gate/up row of
+//            that expert (workgroup b owns rows [b I/256, (b+1) I/256) of every selected
+//            expert: the single token is the same for every expert); the later selection
+//            rounds run while the first slots stream.  The selected experts' down rows of
+//            the H-slice are copied HBM -> LDS (no registers): bf16 by the last two waves
+//            after every gate/up row, so they land during the h exchange; 4-bit by every
+//            wave with each slot.
+//   wait     for the words of h: one per (pair of slots, row of I), two bf16 values each,
+//            polled by the waves with no copies in flight.
 //   phase 3  down rows from LDS against h (bf16, as on every path), one slot per wave and
 //            8 lanes per row; combine (shared first, then j ascending) -> y.
 //
@@ -306,10 +309,11 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 
     // Down rows of this H-slice, slot block j at dyn + j * cpb * 16: chunk c (16 bytes).
     // For NVFP4 a block is the rows' codes followed by their block scales (each contiguous
-    // in HBM for a run of rows).  Wave w copies chunk groups w, w + 8, ...
-    auto load_down = [&](int j, int e) {
+    // in HBM for a run of rows).  Waves w0 .. w0 + nw - 1 copy chunk groups w - w0,
+    // w - w0 + nw, ...
+    auto load_down = [&](int j, int e, int w0, int nw) {
         const int ncq = rows_h * I / 32;
-        for (int g = wave; g < ngrp; g += kWaves) {
+        for (int g = wave - w0; g < ngrp; g += nw) {
             const int c = 64 * g + lane;
             if (c < cpb) {
                 const uint8_t *src;
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     // barrier below, so the 2 MB of router rows are ahead of the shared expert's 9 MB in the
     // memory queues and the logits, on which everything after depends, come back sooner
     // (with 4-bit weights the shared expert is 2.6 MB and holding it back measured slower).
-    if (FMT != 0 && S) load_down(k, E);
+    if (FMT != 0 && S) load_down(k, E, 0, kWaves);
     float4 wv[8];
     u32x2 xv[8];
     if (wave == 0 && b < E) {  // E <= 256: workgroup b computes logit b, if there is one
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     }
     if (FMT == 0) {
         __syncthreads();
-        if (S) load_down(k, E);
+        if (S) load_down(k, E, 0, kWaves);
     }
     if (wave == 0) {
         const int e = b;
@@ -429,8 +433,19 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
             sel[j] = e;
             ordv[j] = m - 1u;
             if (has_row) row_issue<FMT>(a, my_mat, e, i0 + (wave >> 1), rl[j]);
-            load_down(j, e);
+            if (FMT != 0) load_down(j, e, 0, kWaves);
         }
+    }
+    // bf16: the routed down rows are needed only after the h exchange: the last two waves
+    // copy them once every gate/up row has been asked for, so the gate/up rows, on which h
+    // and everything after it wait, are ahead of them in the memory queues; the copies then
+    // land while h is exchanged.  (These waves' own loads return in order, so they take no
+    // part in polling for h.)  With 4-bit weights the down rows are a few KB per slot and
+    // go out with each slot, by every wave (deferring them measured slower).
+    if (FMT == 0 && wave >= kWaves - 2) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; j++)
+            if (j < k) load_down(j, sel[j], kWaves - 2, 2);
     }
     if (wave == 0 && lane == 0) {
         float sum = 0.f;
@@ -464,7 +479,15 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         }
     }
     if (FMT == 1 && wave == 0 && lane < ns) sh.dts[lane] = dts;
-    __syncthreads();  // also completes this workgroup's HBM -> LDS copies
+    if (FMT == 0) {
+        // LDS writes done, then a barrier that does not wait for the down-row copies in flight
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    } else {
+        __syncthreads();  // also completes this workgroup's HBM -> LDS copies
+    }
     for (int q = tid; q < (k + 1) / 2 * npair; q += 512) {
         const int jp = q / npair, p = q - jp * npair, j = 2 * jp;
         const float lo = silu(sh.g[j][p]) * sh.u[j][p];
@@ -498,16 +521,17 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 
     // ---------------- phase 3: down rows from LDS against h, combine
     {
-        constexpr int NH = (kMaxK + 2) / 2 * 1024 / 512;
-        const int nh = (ns + 1) / 2 * I, nq = tid < nh ? (nh - tid + 511) / 512 : 0;
+        constexpr int kPollT = 64 * (FMT == 0 ? kWaves - 2 : kWaves);  // waves with no down-row copies in flight
+        constexpr int NH = ((kMaxK + 2) / 2 * 1024 + kPollT - 1) / kPollT;
+        const int nh = (ns + 1) / 2 * I, nq = tid < kPollT && tid < nh ? (nh - tid + kPollT - 1) / kPollT : 0;
         uint64_t hw[NH];
 #pragma unroll
-        for (int q = 0; q < NH; q++) hw[q] = q < nq ? get_word(a.xh + tid + 512 * q) : 0ull;
-        await_words<NH>(a.xh + tid, 512, nq, hw, tag, a.ctl);
+        for (int q = 0; q < NH; q++) hw[q] = q < nq ? get_word(a.xh + tid + kPollT * q) : 0ull;
+        await_words<NH>(a.xh + tid, kPollT, nq, hw, tag, a.ctl);
 #pragma unroll
         for (int q = 0; q < NH; q++) {
             if (q < nq) {
-                const int wdx = tid + 512 * q, jp = wdx / I, i = wdx - jp * I;
+                const int wdx = tid + kPollT * q, jp = wdx / I, i = wdx - jp * I;
                 sh.hb[(size_t)(2 * jp) * I + i] = (uint16_t)(hw[q] & 0xffffu);
                 if (2 * jp + 1 < ns) sh.hb[(size_t)(2 * jp + 1) * I + i] = (uint16_t)((hw[q] >> 16) & 0xffffu);
             }
