@@ -234,25 +234,27 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 // KS = 1: one workgroup per (touched expert, 64 rows of H): wave w multiplies rows 64 nb +
 // 16 w ... + 15 (MFMA columns) over all of K = I against the expert's h rows, every load of
 // a batch in flight.  KS = 4 (few experts, e.g. a dense layer): one workgroup per (expert,
-// 16 rows), wave w takes the w-th quarter of K and the quarters are summed through LDS, so
-// four times as many waves stream the same rows.  Per-slot outputs o[slot][n] go to the
+// RW rows), wave w takes the w-th quarter of K and the quarters are summed through LDS, so
+// four times as many waves stream the same rows; RW = 8 (MFMA columns 8-15 repeat 0-7 and
+// are not stored) when 16-row workgroups would leave CUs without work.  Per-slot outputs o[slot][n] go to the
 // workspace in fp32.  `cls` as for gate/up.  Thousands of small independent workgroups
 // keep the weight stream busy the way the gate/up pass does.
-template <int FMT, int NMT, int KS>
+template <int FMT, int NMT, int KS, int RW = 16>
 __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int cls, int dense_T, WSet w,
                                                         const uint16_t *__restrict__ h, Plan p,
                                                         float *__restrict__ o, uint16_t *__restrict__ y)
 {
     static_assert(KS == 1 || KS == 4, "K split over the 4 waves or none");
+    static_assert(RW == 16 || RW == 8, "16 or 8 rows per workgroup");
     __shared__ f32x4 red[KS == 4 ? 3 : 1][NMT][64];
-    const int nrb = H / (64 / KS);
+    const int nrb = KS == 1 ? H / 64 : H / RW;
     const int u = blockIdx.x / nrb, nb = blockIdx.x - u * nrb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     // dense_T > 0: a dense layer, one implicit unit of dense_T tokens whose outputs are y
     const int nT = dense_T ? 1 : p.meta[0];
     const int e = dense_T ? E : p.touched[u], base = dense_T ? 0 : p.tbase[u], cnt = dense_T ? dense_T : p.tcount[u];
     if (u >= nT || (cls == 1 && cnt > 16) || (cls == 2 && cnt <= 16)) return;
-    const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * 16 + r;  // MFMA column r of this wave
+    const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * RW + (r % RW);  // MFMA column r of this wave
     const int kw = KS == 1 ? 0 : wave;  // this wave's part of K
     const int nmt = (cnt + 15) >> 4;
     const uint16_t *hr[NMT];
@@ -270,7 +272,9 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
         const uint16_t *Wd = reinterpret_cast<const uint16_t *>(expert_base(w.down, e, E, (size_t)H * I * 2)) +
                              (size_t)row * I;
         const int nch = I / 32, ce = nch * (kw + 1) / KS;
-        constexpr int NB = (NMT == 1 ? 24 : 12) / KS;
+        // KS = 4: 16 (8) chunks per batch, so a dense layer's long rows take two round
+        // trips per wave instead of six
+        constexpr int NB = KS == 1 ? (NMT == 1 ? 24 : 12) : (NMT == 1 ? 16 : 8);
         int c0 = nch * kw / KS;
         for (; c0 + NB <= ce; c0 += NB) {   // full batches: every load issued, no branches
             u32x4 b[NB], a[NMT][NB];
@@ -287,12 +291,22 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                 for (int mt = 0; mt < NMT; mt++)
                     if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i]), as_bf16x8(b[i]), acc[mt]);
         }
-        for (; c0 < ce; c0++) {                // tail
-            const u32x4 b = ld16(Wd + c0 * 32 + g * 8);
+        if (c0 < ce) {                         // the last, partial batch: its loads in flight together
+            u32x4 b[NB], a[NMT][NB];
+#pragma unroll
+            for (int i = 0; i < NB; i++) b[i] = c0 + i < ce ? ld16(Wd + (c0 + i) * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int mt = 0; mt < NMT; mt++)
-                if (NMT == 1 || mt < nmt)
-                    acc[mt] = mfma16x16x32(as_bf16x8(has_tok[mt] ? ld16(hr[mt] + c0 * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u}), as_bf16x8(b), acc[mt]);
+#pragma unroll
+                for (int i = 0; i < NB; i++)
+                    a[mt][i] = (NMT == 1 || mt < nmt) && c0 + i < ce && has_tok[mt] ? ld16(hr[mt] + (c0 + i) * 32 + g * 8)
+                                                                                  : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < NB; i++)
+                if (c0 + i < ce)
+#pragma unroll
+                    for (int mt = 0; mt < NMT; mt++)
+                        if (NMT == 1 || mt < nmt) acc[mt] = mfma16x16x32(as_bf16x8(a[mt][i]), as_bf16x8(b[i]), acc[mt]);
         }
     } else {
         const size_t srow = scale_row_bytes(FMT, I);
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int ti = mt * 16 + 4 * g + i;
-            if ((NMT == 1 || mt < nmt) && ti < cnt) {
+            if ((NMT == 1 || mt < nmt) && ti < cnt && (KS == 1 || r < RW)) {
                 if (dense_T)  // the combine of a dense layer is y = bf16(o): written here
                     y[(size_t)ti * H + row] = (uint16_t)f2bf(acc[mt][i] * ts);
                 else
@@ -448,7 +462,8 @@ static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, in
                                                          plan, h);
 }
 
-// Split K over the waves when 64-row workgroups would leave most CUs idle.
+// Split K over the waves when 64-row workgroups would leave most CUs idle, and take 8 rows
+// per workgroup when 16-row ones would still number fewer than the CUs.
 template <int FMT, int NMT>
 static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, int cls, const uint16_t *h,
                         const Plan &plan, float *o, uint16_t *y, hipStream_t st)
@@ -457,9 +472,12 @@ static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, int 
     if (maxU * (s.H / 64) >= 512)
         gemv_down_kernel<FMT, NMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, cls, dense_T, w, h,
                                                                                   plan, o, y);
-    else
+    else if (maxU * (s.H / 16) >= 256)
         gemv_down_kernel<FMT, NMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, cls, dense_T, w, h,
                                                                                   plan, o, y);
+    else
+        gemv_down_kernel<FMT, NMT, 4, 8><<<(unsigned)(maxU * (s.H / 8)), 256, 0, st>>>(s.H, s.I, s.E, cls, dense_T, w,
+                                                                                    h, plan, o, y);
 }
 
 // With routed experts the plan lists units of at most 16 tokens (an expert with more is
