@@ -396,7 +396,8 @@ def main():
         achieved = bytes_per_call / (avg_call_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
-                "kernel": ("flint_moe_layer (dense: plan, gate/up, down, combine kernels)" if E == 0 else
+                "kernel": ("dense1_kernel (the whole dense layer in one persistent launch)" if E == 0 and T == 1 else
+                           "flint_moe_layer (dense: gate/up and down kernels)" if E == 0 else
                            "decode1_kernel (one persistent launch per layer; chain call time / layers)"
                            if chain else
                            "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else

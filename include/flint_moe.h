@@ -172,7 +172,10 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
    grouped-GEMM path (T > 32) each per-slot output o is also rounded to bf16 before the
    combine, while the streaming path (T <= 32) combines o in fp32.
    topk_ids/topk_w/offsets/sorted_assign/assign_pos are the outputs of route and
-   permute for the same T.  y: bf16 [T][H]. */
+   permute for the same T.  y: bf16 [T][H].
+   A dense layer (n_experts == 0) with one bf16 token, 512 <= I <= 4096 and H <= 2048
+   runs as one persistent launch that exchanges h through the workspace head, like
+   flint_moe_layer's single-token launch below (same device and head requirements). */
 int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
                       const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                       const int32_t *offsets, const int32_t *sorted_assign,
@@ -185,7 +188,8 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
    launch of one workgroup per CU (on a device with at least 256 CUs) whose workgroups
    exchange logits and h through tagged words at the start of the workspace (see
    flint_moe_workspace_init); it rounds h to bf16 like the other paths and combines the
-   per-slot outputs in fp32.  A wait there
+   per-slot outputs in fp32; a dense layer's single bf16 token likewise (see
+   flint_moe_forward).  A wait there
    that runs out (it cannot on a device with a CU per workgroup) sets the word at byte 4
    of the workspace to 1. */
 int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,

@@ -303,6 +303,8 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
     if (ws_bytes < L.total) return FLINT_ERR_WORKSPACE;
     const Plan plan = plan_view(ws, L, s);
     hipStream_t st = (hipStream_t)stream;
+    if (dense && T == 1 && dense1_supported(s, weights->format))
+        return hip_status(launch_dense1(s, wset_of(weights), x, y, (char *)ws + L.sync, st));
     if (!dense || T > kGemvMaxT) {  // the streaming kernels take a dense layer's plan as implicit
         rc = hip_status(launch_plan(s, T, dense ? nullptr : offsets, plan, st));
         if (rc) return rc;
@@ -347,6 +349,8 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     hipStream_t st = (hipStream_t)stream;
     const Plan plan = plan_view(ws, L, s);
     if (dense) {
+        if (T == 1 && dense1_supported(s, weights->format))
+            return hip_status(launch_dense1(s, wset_of(weights), x, y, b + L.sync, st));
         if (T > kGemvMaxT) {  // the streaming kernels take a dense layer's plan as implicit
             rc = hip_status(launch_plan(s, T, nullptr, plan, st));
             if (rc) return rc;

@@ -105,6 +105,11 @@ hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, cons
                           const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
                           int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
                           hipStream_t st);
+// Dense SwiGLU layer (E = 0, the one expert held as the shared expert), one bf16 token, in
+// one persistent launch (decode1.hip); same head and CU check as launch_decode1.
+bool dense1_supported(const Shape &s, int fmt);
+hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint16_t *y, void *head,
+                         hipStream_t st);
 // One token through L layers, one single-token launch per layer: layer l + 1's token is
 // y_l, or bf16(x_l + y_l) with `residual`, handed on through the workspace head.  x = null
 // starts from the token a previous call left there (`hand_on`).  y: [L][H]; ids, tw: [L][k],

@@ -595,6 +595,100 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     }
 }
 
+// ---------------------------------------------------------------- dense layer, one token
+// A dense SwiGLU layer (no router, the one expert held as the shared expert: the dense
+// layers of the same model, qantcore.space review, section 01) for one token, bf16, in one
+// launch of one workgroup per CU.  h travels as W = I / 2 exchange words, word q holding
+// bf16 h[2q] (low half) and h[2q + 1]; workgroup b owns words [b W / 256, (b + 1) W / 256)
+// (1 to 8 of them) and the down rows of its H-slice.
+//   waves 0-7   one word each: the gate and up rows 2q and 2q + 1 (4 rows of H in flight
+//               per lane), then the word; then they poll all W words and write h to LDS.
+//   waves 8, 9  copy the down rows of the slice HBM -> LDS behind the row loads, and
+//               take no part in polling (a wave's loads return in order).
+//   all         down row n = wave of the slice against h from LDS -> y.
+// The launch counter advances once workgroup 0 has seen every word: each was written
+// after its writer read the counter, so every workgroup has read it.
+constexpr int kDenseRowWaves = 8, kDenseWaves = kDenseRowWaves + 2, kDenseMaxI = 4096;
+
+__global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];  // down rows, bf16 [rows_h][I]
+    __shared__ __attribute__((aligned(16))) uint16_t hb[kDenseMaxI];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, b = blockIdx.x;
+    const int H = a.H, I = a.I, W = I / 2;
+    const int rows_h = H / kG, n0 = b * rows_h;
+    const int q0 = b * W / kG, nq = (b + 1) * W / kG - q0;
+
+    // The row waves' loads go out first; the copy waves start after a barrier that waits
+    // for no load, so the gate/up rows, on which h and the exchange wait, are ahead of the
+    // down rows in the memory queues and the down rows land while h is exchanged.
+    const bool rows = wave < kDenseRowWaves && wave < nq;
+    const int i = 2 * (q0 + wave);
+    u32x4 v[4][kMaxXC], xb[kMaxXC];
+    if (rows) {
+        const uint16_t *rp[4] = {
+            reinterpret_cast<const uint16_t *>(a.w.gate.shared) + (size_t)i * H,
+            reinterpret_cast<const uint16_t *>(a.w.up.shared) + (size_t)i * H,
+            reinterpret_cast<const uint16_t *>(a.w.gate.shared) + (size_t)(i + 1) * H,
+            reinterpret_cast<const uint16_t *>(a.w.up.shared) + (size_t)(i + 1) * H};
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+#pragma unroll
+            for (int c = 0; c < kMaxXC; c++)
+                if (lane + 64 * c < H / 8) v[r][c] = ld16(rp[r] + 8 * (lane + 64 * c));
+#pragma unroll
+        for (int c = 0; c < kMaxXC; c++)
+            xb[c] = lane + 64 * c < H / 8 ? ld16(a.x + 8 * (lane + 64 * c)) : u32x4{0, 0, 0, 0};
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // read after the row loads, whose data the dots wait for anyway (a wave's loads return
+    // in order), so that nothing before the barrier waits for a load
+    const uint32_t tag = wave < kDenseRowWaves
+        ? __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
+    if (wave >= kDenseRowWaves) {
+        const int cpb = rows_h * I / 8;  // 16-byte chunks of the slice's down rows
+        const uint8_t *src = a.w.down.shared + (size_t)n0 * I * 2;
+        for (int g = wave - kDenseRowWaves; 64 * g < cpb; g += kDenseWaves - kDenseRowWaves) {
+            const int c = 64 * g + lane;
+            if (c < cpb) lds_load16(src + 16 * c, dyn + (size_t)64 * g * 16);
+        }
+    } else if (rows) {
+        float d[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < kMaxXC; c++)
+                if (lane + 64 * c < H / 8) acc = dot8_bf16(v[r][c], xb[c], acc);
+            d[r] = wave_sum(acc);
+        }
+        if (lane == 0) put_h2(a.xh + q0 + wave, tag, silu(d[0]) * d[1], silu(d[2]) * d[3]);
+    }
+    if (wave < kDenseRowWaves) {
+        constexpr int kPollT = 64 * kDenseRowWaves, NH = kDenseMaxI / 2 / kPollT;
+        const int nw = tid < W ? (W - tid + kPollT - 1) / kPollT : 0;
+        uint64_t hw[NH];
+#pragma unroll
+        for (int q = 0; q < NH; q++) hw[q] = q < nw ? get_word(a.xh + tid + kPollT * q) : 0ull;
+        await_words<NH>(a.xh + tid, kPollT, nw, hw, tag, a.ctl);
+#pragma unroll
+        for (int q = 0; q < NH; q++)
+            if (q < nw) reinterpret_cast<uint32_t *>(hb)[tid + kPollT * q] = (uint32_t)hw[q];
+    }
+    __syncthreads();  // h in LDS; the copy waves' down rows have landed
+    if (b == 0 && tid == 0) __hip_atomic_store(a.ctl + kCtlEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave < rows_h) {
+        const uint8_t *row = dyn + (size_t)wave * I * 2;
+        float acc = 0.f;
+        for (int c = lane; c < I / 8; c += 64)
+            acc = dot8_bf16(*reinterpret_cast<const u32x4 *>(row + 16 * c), *reinterpret_cast<const u32x4 *>(hb + 8 * c), acc);
+        acc = wave_sum(acc);
+        if (lane == 0) a.y[n0 + wave] = (uint16_t)f2bf(acc);
+    }
+}
+
 }  // namespace
 
 // LDS for the down rows of one workgroup's H-slice, all k + S experts.
@@ -668,6 +762,30 @@ hipError_t launch_decode_chain(const Shape &s, const WSet *w, const float *const
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+bool dense1_supported(const Shape &s, int fmt)
+{
+    return fmt == 0 && s.E == 0 && s.S == 1 && s.H % kG == 0 && s.H <= 2048 &&  // <= 8 down rows per workgroup
+           s.I % 8 == 0 && s.I >= 2 * kG && s.I <= kDenseMaxI &&              // 1..8 h words per workgroup
+           (size_t)(s.H / kG) * s.I * 2 <= 128 * 1024 && device_cus() >= kG;
+}
+
+hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint16_t *y, void *head,
+                         hipStream_t st)
+{
+    char *hb = static_cast<char *>(head);
+    D1Args a{};
+    a.H = s.H;
+    a.I = s.I;
+    a.S = 1;
+    a.w = w;
+    a.x = x;
+    a.y = y;
+    a.ctl = reinterpret_cast<uint32_t *>(hb);
+    a.xh = reinterpret_cast<uint64_t *>(hb + kXHOff);
+    dense1_kernel<<<kG, 64 * kDenseWaves, (size_t)(s.H / kG) * s.I * 2, st>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace flint

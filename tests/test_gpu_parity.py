@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 import sparse_moe_transformer_wave_amd as fm  # noqa: E402
 from sparse_moe_transformer_wave_amd import datagen as dg  # noqa: E402
-from moe_cases import Case, check_forward, check_routing  # noqa: E402
+from moe_cases import Case, check_forward, check_routing, to_host  # noqa: E402
 
 
 def _say(msg):
@@ -202,7 +202,7 @@ def test_full_prefill_nvfp4_8192():
 
 
 # ---------------------------------------------------------------- dense SwiGLU layer
-def _dense_check(T, H, I, fmt, layer=0, tokens=None, three_call=False):
+def _dense_check(T, H, I, fmt, layer=0, tokens=None, three_call=False, ws=None):
     """n_experts = 0: y = bf16(down(silu(gate x) * up x)) with the shared-expert pointers,
     against the reference's SwiGLU expert (sum in fp64) for each checked token."""
     _say("dense T=%d H=%d I=%d fmt=%d" % (T, H, I, fmt))
@@ -211,7 +211,8 @@ def _dense_check(T, H, I, fmt, layer=0, tokens=None, three_call=False):
     w.gate = w.up = w.down = None
     w.gate_sf = w.up_sf = w.down_sf = w.gate_ts = w.up_ts = w.down_ts = None
     y = torch.zeros((T, H), dtype=torch.int16, device="cuda")
-    ws = c.workspace()
+    if ws is None:
+        ws = c.workspace()
     if three_call:
         fm.forward(c.desc, w, T, c.d_x, None, None, None, None, None, y, ws)
     else:
@@ -244,6 +245,36 @@ def test_dense_tiny_three_call_and_nvfp4():
 @pytest.mark.parametrize("T", [1, 8, 32])
 def test_dense_full_decode(T):
     _dense_check(T, 2048, 4096, fm.WFMT_BF16, layer=1)
+
+
+@pytest.mark.parametrize("H,I", [(2048, 1152), (512, 512), (1024, 2176), (256, 4096), (2048, 640)])
+def test_dense_single_token_shapes(H, I):
+    """One bf16 token of a dense layer with 512 <= I <= 4096 runs as one persistent launch:
+    1 to 8 h words per workgroup (uneven for I = 640, 1152, 2176), 1 to 8 down rows each."""
+    _dense_check(1, H, I, fm.WFMT_BF16, layer=2)
+
+
+def test_dense_and_moe_single_token_share_a_workspace():
+    """The dense and the MoE single-token launches take turns on one workspace (the launch
+    counter and the tagged words carry over from one to the other), through
+    flint_moe_layer and flint_moe_forward."""
+    c = Case(1, 2048, 768, 256, 6, layer=3)
+    dd = fm.desc(2048, 4096, n_experts=0, top_k=0, n_shared=1)
+    ws = torch.empty(max(fm.workspace_bytes(c.desc, 1), fm.workspace_bytes(dd, 1)),
+                     dtype=torch.uint8, device="cuda")
+    fm.workspace_init(ws)
+    c.upload()
+    for rep in range(3):
+        _dense_check(1, 2048, 4096, fm.WFMT_BF16, layer=rep, three_call=rep == 1, ws=ws)
+        out = c.alloc_out()
+        routing = {k: out[k] for k in ("logits", "topk_ids", "topk_w", "counts", "offsets",
+                                       "sorted_assign", "assign_pos")}
+        fm.layer(c.desc, c.weights, 1, c.d_x, c.d_Wr, c.d_bias, out["y"], ws, routing)
+        torch.cuda.synchronize()
+        g = to_host(out, c)
+        w64 = check_routing(c, g, {})
+        check_forward(c, g, w64, None)
+    assert int(ws[4:8].view(torch.int32).item()) == 0  # no wait ran out
 
 
 def test_dense_full_prefill_8192():
