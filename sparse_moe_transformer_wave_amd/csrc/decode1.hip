@@ -603,12 +603,12 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 // (1 to 8 of them) and the down rows of its H-slice.
 //   waves 0-7   one word each: the gate and up rows 2q and 2q + 1 (4 rows of H in flight
 //               per lane), then the word; then they poll all W words and write h to LDS.
-//   waves 8, 9  copy the down rows of the slice HBM -> LDS behind the row loads, and
+//   waves 8-11  copy the down rows of the slice HBM -> LDS behind the row loads, and
 //               take no part in polling (a wave's loads return in order).
 //   all         down row n = wave of the slice against h from LDS -> y.
 // The launch counter advances once workgroup 0 has seen every word: each was written
 // after its writer read the counter, so every workgroup has read it.
-constexpr int kDenseRowWaves = 8, kDenseWaves = kDenseRowWaves + 2, kDenseMaxI = 4096;
+constexpr int kDenseRowWaves = 8, kDenseWaves = kDenseRowWaves + 4, kDenseMaxI = 4096;
 
 __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
 {
