@@ -73,6 +73,12 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
     for (int mt = 0; mt < NMT; mt++) has_tok[mt] = mt * 16 + r < cnt;
     const int i0 = rb * 8 * RG;             // first row of I of this unit
     const WMat &wm = (r < 8) ? w.gate : w.up;  // gate row (lanes r < 8) or up row (r >= 8)
+    // NVFP4 tensor scales, asked for with the weights so the epilogue does not wait for them
+    float tsg = 1.f, tsu = 1.f;
+    if (FMT == 1) {
+        tsg = expert_ts(w.gate, e, E);
+        tsu = expert_ts(w.up, e, E);
+    }
     f32x4 acc[RG][NMT];
 #pragma unroll
     for (int q = 0; q < RG; q++)
@@ -209,11 +215,6 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 #pragma unroll
             for (int i = 0; i < 4; i++) red[wave][q][mt][lane][i] = acc[q][mt][i];
     __syncthreads();
-    float tsg = 1.f, tsu = 1.f;
-    if (FMT == 1) {
-        tsg = expert_ts(w.gate, e, E);
-        tsu = expert_ts(w.up, e, E);
-    }
     // D[m][n] sits in lane 16 (m / 4) + n, element m % 4; g in columns 0-7, u in 8-15.
     for (int j = tid; j < RG * nmt * 128; j += 256) {
         const int q = j / (nmt * 128), jj = j - q * nmt * 128;
