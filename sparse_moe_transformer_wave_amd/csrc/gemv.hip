@@ -54,9 +54,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     // The unit's plan entry loads together with the unit count (one round trip), then the
     // token indices of the A rows together with the first weights (one more).
-    // a dense layer's plan is implicit: one unit, the T tokens in slots 0 .. T - 1
-    const int nT = dense ? 1 : p.meta[0];
-    const int e = dense ? E : p.touched[u], base = dense ? 0 : p.tbase[u], cnt = dense ? T : p.tcount[u];
+    // a dense layer's plan is implicit: unit u holds tokens 16 u .. 16 u + 15 in the same slots
+    const int nT = dense ? (T + 15) / 16 : p.meta[0];
+    const int e = dense ? E : p.touched[u], base = dense ? 16 * u : p.tbase[u], cnt = dense ? min(16, T - 16 * u) : p.tcount[u];
     if (u >= nT || (cls == 1 && cnt > 16) || (cls == 2 && cnt <= 16)) return;
     int tix[NMT];
 #pragma unroll
@@ -251,9 +251,9 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
     const int nrb = KS == 1 ? H / 64 : H / RW;
     const int u = blockIdx.x / nrb, nb = blockIdx.x - u * nrb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-    // dense_T > 0: a dense layer, one implicit unit of dense_T tokens whose outputs are y
-    const int nT = dense_T ? 1 : p.meta[0];
-    const int e = dense_T ? E : p.touched[u], base = dense_T ? 0 : p.tbase[u], cnt = dense_T ? dense_T : p.tcount[u];
+    // dense_T > 0: a dense layer of dense_T tokens, unit u = tokens 16 u .. 16 u + 15, outputs y
+    const int nT = dense_T ? (dense_T + 15) / 16 : p.meta[0];
+    const int e = dense_T ? E : p.touched[u], base = dense_T ? 16 * u : p.tbase[u], cnt = dense_T ? min(16, dense_T - 16 * u) : p.tcount[u];
     if (u >= nT || (cls == 1 && cnt > 16) || (cls == 2 && cnt <= 16)) return;
     const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * RW + (r % RW);  // MFMA column r of this wave
     const int kw = KS == 1 ? 0 : wave;  // this wave's part of K
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
             const int ti = mt * 16 + 4 * g + i;
             if ((NMT == 1 || mt < nmt) && ti < cnt && (KS == 1 || r < RW)) {
                 if (dense_T)  // the combine of a dense layer is y = bf16(o): written here
-                    y[(size_t)ti * H + row] = (uint16_t)f2bf(acc[mt][i] * ts);
+                    y[(size_t)(base + ti) * H + row] = (uint16_t)f2bf(acc[mt][i] * ts);
                 else
                     o[(size_t)(base + ti) * H + row] = acc[mt][i] * ts;
             }
@@ -483,9 +483,10 @@ static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, int 
 
 // With routed experts the plan lists units of at most 16 tokens (an expert with more is
 // split; in practice the shared expert once T > 16), so one launch of the one-tile
-// kernels covers every unit.  A dense layer (E = 0) keeps its single unit whole, so its
-// weights are read once: the two-tile kernels for T > 16.  Its plan is implicit (no plan
-// launch) and its down pass writes y (no combine launch).
+// kernels covers every unit.  A dense layer (E = 0) is split the same way, so for T > 16
+// its weights are read once per unit; one unit of two token tiles measured slower (its
+// workgroups read twice the activations with twice the registers).  Its plan is implicit
+// (no plan launch) and its down pass writes y (no combine launch).
 template <int FMT>
 static void launch_stream(const Shape &s, const WSet &w, int64_t T, const uint16_t *x,
                           const float *topk_w, const int32_t *sa, const int32_t *ap,
@@ -493,13 +494,8 @@ static void launch_stream(const Shape &s, const WSet &w, int64_t T, const uint16
 {
     const int maxU = (int)(std::min<int64_t>(T * s.k, s.E) + (T * s.k + kUnitRows - 1) / kUnitRows +
                            (int64_t)s.S * ((T + kUnitRows - 1) / kUnitRows));
-    if (s.E > 0 || T <= 16) {
-        launch_gateup<FMT, 1>(s, w, T, maxU, 0, x, sa, plan, h, st);
-        launch_down<FMT, 1>(s, w, T, maxU, 0, h, plan, o, y, st);
-    } else {
-        launch_gateup<FMT, 2>(s, w, T, 1, 0, x, sa, plan, h, st);
-        launch_down<FMT, 2>(s, w, T, 1, 0, h, plan, o, y, st);
-    }
+    launch_gateup<FMT, 1>(s, w, T, maxU, 0, x, sa, plan, h, st);
+    launch_down<FMT, 1>(s, w, T, maxU, 0, h, plan, o, y, st);
     if (s.E == 0) return;
     const int nthreads = (int)T * (s.H / 8);
     gemv_combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o, topk_w, ap, y);
