@@ -12,7 +12,8 @@ Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant kernel (b
 flops per launch over its measured duration) and the reference's single-core CPU rate on
 a bounded sample.  --config picks another workload: decode_t8, decode_t32, prefill,
 prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32, nvfp4_prefill, int4_t1, int4_t8, int4_t32, int4_prefill, and the dense SwiGLU layer
-(no router, I = 4096) at dense_t1, dense_t32, dense_prefill; chain_t1 and nvfp4_chain_t1
+(no router, I = 4096) at dense_t1, dense_t32, dense_prefill (and nvfp4_dense_t1, int4_dense_t1
+with 4-bit weights); chain_t1 and nvfp4_chain_t1
 run the single token through all 47 layers with one flint_moe_decode_chain call (token of
 layer l + 1 = bf16(x_l + y_l), formed in the kernel of layer l).
 """
@@ -54,6 +55,10 @@ CONFIGS = {
     "dense_t1": dict(T=1, fmt=0, layers=16, zipf=False, dense=True),
     "dense_t32": dict(T=32, fmt=0, layers=16, zipf=False, dense=True),
     "dense_prefill": dict(T=8192, fmt=0, layers=1, zipf=False, dense=True),
+    # the same dense layer's single token with 4-bit weights (48 layers: 680 MB, more than
+    # the last-level cache)
+    "nvfp4_dense_t1": dict(T=1, fmt=1, layers=48, zipf=False, dense=True),
+    "int4_dense_t1": dict(T=1, fmt=2, layers=48, zipf=False, dense=True),
 }
 
 
@@ -139,17 +144,19 @@ def build_layer(torch, fm, dg, l, fmt, zipf, shp):
             d["weights"] = fm.Weights(0, d["gate"], d["up"], d["down"], d["gate"][E], d["up"][E],
                                       d["down"][E])
     elif fmt == 2:
-        assert E > 0, "dense INT4 layers are not part of the benchmark"
         for name, kind, N, K in kinds:
             q = torch.empty((E + S, N, K // 2), dtype=torch.uint8, device="cuda")
             sc = torch.empty((E + S, N, K // 128), dtype=torch.int16, device="cuda")
             dg.device_int4(q, sc, E + S, N, K, 0, dg.stream_id(l, kind, 0), dg.W_STD)
             d["q_" + name], d["sc_" + name] = q, sc
-        d["weights"] = fm.Weights(
-            2, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
-            d["sc_gate"], d["sc_up"], d["sc_down"], d["sc_gate"][E], d["sc_up"][E], d["sc_down"][E])
+        if E == 0:  # dense layer: the shared expert's pointers only
+            d["weights"] = fm.Weights(2, None, None, None, d["q_gate"][0], d["q_up"][0], d["q_down"][0],
+                                      None, None, None, d["sc_gate"][0], d["sc_up"][0], d["sc_down"][0])
+        else:
+            d["weights"] = fm.Weights(
+                2, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
+                d["sc_gate"], d["sc_up"], d["sc_down"], d["sc_gate"][E], d["sc_up"][E], d["sc_down"][E])
     else:
-        assert E > 0, "dense NVFP4 layers are not part of the benchmark"
         scratch = torch.empty(E + S, dtype=torch.int32, device="cuda")
         for name, kind, N, K in kinds:
             q = torch.empty((E + S, N, K // 2), dtype=torch.uint8, device="cuda")
@@ -160,10 +167,15 @@ def build_layer(torch, fm, dg, l, fmt, zipf, shp):
         sh_ts = torch.stack([d["ts_gate"][E], d["ts_up"][E], d["ts_down"][E]]).contiguous()
         sh_ts = torch.cat([sh_ts, torch.zeros(1, device="cuda")])
         d["sh_ts"] = sh_ts
-        d["weights"] = fm.Weights(
-            1, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
-            d["sf_gate"], d["sf_up"], d["sf_down"], d["sf_gate"][E], d["sf_up"][E],
-            d["sf_down"][E], d["ts_gate"], d["ts_up"], d["ts_down"], sh_ts)
+        if E == 0:  # dense layer: the shared expert's pointers only
+            d["weights"] = fm.Weights(
+                1, None, None, None, d["q_gate"][0], d["q_up"][0], d["q_down"][0], None, None, None,
+                d["sf_gate"][0], d["sf_up"][0], d["sf_down"][0], None, None, None, sh_ts)
+        else:
+            d["weights"] = fm.Weights(
+                1, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
+                d["sf_gate"], d["sf_up"], d["sf_down"], d["sf_gate"][E], d["sf_up"][E],
+                d["sf_down"][E], d["ts_gate"], d["ts_up"], d["ts_down"], sh_ts)
     return d
 
 
@@ -245,17 +257,29 @@ def cpu_result(T, done, n_layers, t_used, what):
 
 
 def cpu_baseline_dense(cfg, budget_s, x, H, I, n_layers):
-    """The reference's SwiGLU expert (the dense layer) for each token, layers cycled."""
+    """The reference's SwiGLU expert (the dense layer) for each token, layers cycled; 4-bit
+    weights are quantised on the host by the reference's own quantisers."""
     import numpy as np
 
     import oracle
     from sparse_moe_transformer_wave_amd import datagen as dg
+    fmt = cfg["fmt"]
     layers = []
     for l in range(n_layers):
-        arrays = {name: dg.normal_bf16(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD)[None]
-                  for name, kind, shape in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
-                                            ("down", dg.KIND_DOWN, (H, I)))}
-        layers.append(oracle.Experts(oracle.FMT_BF16, H, I, arrays))
+        arrays = {}
+        for name, kind, shape in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
+                                  ("down", dg.KIND_DOWN, (H, I))):
+            if fmt == 0:
+                arrays[name] = dg.normal_bf16(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD)[None]
+            elif fmt == 1:
+                q, sb, st = oracle.nvfp4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD))
+                arrays["q_" + name], arrays["sb_" + name] = q[None], sb[None]
+                arrays["st_" + name] = np.array([st], dtype=np.float32)
+            else:
+                q, sb = oracle.int4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD))
+                arrays["q_" + name], arrays["sb_" + name] = q[None], sb[None]
+        fmt_o = (oracle.FMT_BF16, oracle.FMT_NVFP4, oracle.FMT_INT4)[fmt]
+        layers.append(oracle.Experts(fmt_o, H, I, arrays))
     xf = dg.bf16_bits_to_f32(x).astype(np.float64)
     done, t_used = 0, 0.0
     while t_used < budget_s:
@@ -265,7 +289,8 @@ def cpu_baseline_dense(cfg, budget_s, x, H, I, n_layers):
             oracle.expert_ffn(ex, 0, xf[t])
         t_used += time.perf_counter() - t0
         done += 1
-    return cpu_result(x.shape[0], done, n_layers, t_used, "dense SwiGLU layer")
+    return cpu_result(x.shape[0], done, n_layers, t_used, ("dense SwiGLU layer", "dense SwiGLU layer, NVFP4 weights",
+                                                          "dense SwiGLU layer, INT4 weights")[fmt])
 
 
 def main():

@@ -173,9 +173,10 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
    combine, while the streaming path (T <= 32) combines o in fp32.
    topk_ids/topk_w/offsets/sorted_assign/assign_pos are the outputs of route and
    permute for the same T.  y: bf16 [T][H].
-   A dense layer (n_experts == 0) with one bf16 token, 512 <= I <= 4096 and H <= 2048
-   runs as one persistent launch that exchanges h through the workspace head, like
-   flint_moe_layer's single-token launch below (same device and head requirements). */
+   A dense layer (n_experts == 0) with one token, 512 <= I <= 4096 and H <= 2048 (any
+   weight format) runs as one persistent launch that exchanges h through the workspace
+   head, like flint_moe_layer's single-token launch below (same device and head
+   requirements). */
 int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
                       const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                       const int32_t *offsets, const int32_t *sorted_assign,

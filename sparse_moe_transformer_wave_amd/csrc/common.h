@@ -105,8 +105,9 @@ hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, cons
                           const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
                           int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
                           hipStream_t st);
-// Dense SwiGLU layer (E = 0, the one expert held as the shared expert), one bf16 token, in
-// one persistent launch (decode1.hip); same head and CU check as launch_decode1.
+// Dense SwiGLU layer (E = 0, the one expert held as the shared expert), one token in any
+// weight format, in one persistent launch (decode1.hip); same head and CU check as
+// launch_decode1.
 bool dense1_supported(const Shape &s, int fmt);
 hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint16_t *y, void *head,
                          hipStream_t st);

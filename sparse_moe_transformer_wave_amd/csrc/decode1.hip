@@ -597,48 +597,58 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 
 // ---------------------------------------------------------------- dense layer, one token
 // A dense SwiGLU layer (no router, the one expert held as the shared expert: the dense
-// layers of the same model, qantcore.space review, section 01) for one token, bf16, in one
+// layers of the same model, qantcore.space review, section 01) for one token, in one
 // launch of one workgroup per CU.  h travels as W = I / 2 exchange words, word q holding
 // bf16 h[2q] (low half) and h[2q + 1]; workgroup b owns words [b W / 256, (b + 1) W / 256)
 // (1 to 8 of them) and the down rows of its H-slice.
 //   waves 0-7   one word each: the gate and up rows 2q and 2q + 1 (4 rows of H in flight
 //               per lane), then the word; then they poll all W words and write h to LDS.
-//   waves 8-11  copy the down rows of the slice HBM -> LDS behind the row loads, and
-//               take no part in polling (a wave's loads return in order).
+//   waves 8-11  copy the down rows of the slice HBM -> LDS behind the row loads (4-bit:
+//               the rows' codes, then their scales), and take no part in polling (a
+//               wave's loads return in order).
 //   all         down row n = wave of the slice against h from LDS -> y.
 // The launch counter advances once workgroup 0 has seen every word: each was written
 // after its writer read the counter, so every workgroup has read it.
 constexpr int kDenseRowWaves = 8, kDenseWaves = kDenseRowWaves + 4, kDenseMaxI = 4096;
 
+template <int FMT>
 __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];  // down rows, bf16 [rows_h][I]
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];  // down rows of the slice
     __shared__ __attribute__((aligned(16))) uint16_t hb[kDenseMaxI];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, b = blockIdx.x;
     const int H = a.H, I = a.I, W = I / 2;
     const int rows_h = H / kG, n0 = b * rows_h;
     const int q0 = b * W / kG, nq = (b + 1) * W / kG - q0;
+    const size_t srow = scale_row_bytes(FMT, I);  // down row scale bytes (4-bit)
 
     // The row waves' loads go out first; the copy waves start after a barrier that waits
     // for no load, so the gate/up rows, on which h and the exchange wait, are ahead of the
     // down rows in the memory queues and the down rows land while h is exchanged.
     const bool rows = wave < kDenseRowWaves && wave < nq;
     const int i = 2 * (q0 + wave);
-    u32x4 v[4][kMaxXC], xb[kMaxXC];
+    RowLoad<FMT> rl[4];  // gate i, up i, gate i + 1, up i + 1
+    u32x4 xb[kMaxXC];
+    float xf[32];
     if (rows) {
-        const uint16_t *rp[4] = {
-            reinterpret_cast<const uint16_t *>(a.w.gate.shared) + (size_t)i * H,
-            reinterpret_cast<const uint16_t *>(a.w.up.shared) + (size_t)i * H,
-            reinterpret_cast<const uint16_t *>(a.w.gate.shared) + (size_t)(i + 1) * H,
-            reinterpret_cast<const uint16_t *>(a.w.up.shared) + (size_t)(i + 1) * H};
 #pragma unroll
-        for (int r = 0; r < 4; r++)
+        for (int r = 0; r < 4; r++) row_issue<FMT>(a, (r & 1) ? a.w.up : a.w.gate, 0, i + (r >> 1), rl[r]);
+        if (FMT == 0) {
 #pragma unroll
             for (int c = 0; c < kMaxXC; c++)
-                if (lane + 64 * c < H / 8) v[r][c] = ld16(rp[r] + 8 * (lane + 64 * c));
+                xb[c] = lane + 64 * c < H / 8 ? ld16(a.x + 8 * (lane + 64 * c)) : u32x4{0, 0, 0, 0};
+        } else {
 #pragma unroll
-        for (int c = 0; c < kMaxXC; c++)
-            xb[c] = lane + 64 * c < H / 8 ? ld16(a.x + 8 * (lane + 64 * c)) : u32x4{0, 0, 0, 0};
+            for (int q = 0; q < 4; q++) {
+                u32x4 v = (lane < H / 32) ? ld16(a.x + 32 * lane + 8 * q) : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t vj = v[j];
+                    xf[8 * q + 2 * j] = bf2f(vj & 0xffffu);
+                    xf[8 * q + 2 * j + 1] = bf2f(vj >> 16);
+                }
+            }
+        }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
@@ -648,22 +658,19 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
     const uint32_t tag = wave < kDenseRowWaves
         ? __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
     if (wave >= kDenseRowWaves) {
-        const int cpb = rows_h * I / 8;  // 16-byte chunks of the slice's down rows
-        const uint8_t *src = a.w.down.shared + (size_t)n0 * I * 2;
+        const size_t drow = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2;  // code (or bf16) bytes per row
+        const int ncq = (int)(rows_h * drow / 16);                      // 16-byte chunks of them
+        const int cpb = ncq + (int)(rows_h * srow / 16);
+        const uint8_t *src = a.w.down.shared + (size_t)n0 * drow;
+        const uint8_t *ssrc = FMT == 0 ? nullptr : a.w.down.sf_shared + (size_t)n0 * srow;
         for (int g = wave - kDenseRowWaves; 64 * g < cpb; g += kDenseWaves - kDenseRowWaves) {
             const int c = 64 * g + lane;
-            if (c < cpb) lds_load16(src + 16 * c, dyn + (size_t)64 * g * 16);
+            if (c < cpb) lds_load16(c < ncq ? src + 16 * c : ssrc + 16 * (c - ncq), dyn + (size_t)64 * g * 16);
         }
     } else if (rows) {
         float d[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < kMaxXC; c++)
-                if (lane + 64 * c < H / 8) acc = dot8_bf16(v[r][c], xb[c], acc);
-            d[r] = wave_sum(acc);
-        }
+        for (int r = 0; r < 4; r++) d[r] = row_dot<FMT>(a, rl[r], xb, xf);
         if (lane == 0) put_h2(a.xh + q0 + wave, tag, silu(d[0]) * d[1], silu(d[2]) * d[3]);
     }
     if (wave < kDenseRowWaves) {
@@ -680,11 +687,32 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
     __syncthreads();  // h in LDS; the copy waves' down rows have landed
     if (b == 0 && tid == 0) __hip_atomic_store(a.ctl + kCtlEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (wave < rows_h) {
-        const uint8_t *row = dyn + (size_t)wave * I * 2;
         float acc = 0.f;
-        for (int c = lane; c < I / 8; c += 64)
-            acc = dot8_bf16(*reinterpret_cast<const u32x4 *>(row + 16 * c), *reinterpret_cast<const u32x4 *>(hb + 8 * c), acc);
+        if (FMT == 0) {
+            const uint8_t *row = dyn + (size_t)wave * I * 2;
+            for (int c = lane; c < I / 8; c += 64)
+                acc = dot8_bf16(*reinterpret_cast<const u32x4 *>(row + 16 * c), *reinterpret_cast<const u32x4 *>(hb + 8 * c), acc);
+        } else {
+            // 16-element blocks c: 8 code bytes against 16 bf16 h values, times the block's
+            // E4M3 scale (NVFP4) or the bf16 scale of its 128-column group (INT4)
+            const uint8_t *qrow = dyn + (size_t)wave * (I / 2);
+            const uint8_t *sf = dyn + (size_t)rows_h * (I / 2) + (size_t)wave * srow;
+            for (int c = lane; c < I / 16; c += 64) {
+                const u32x2 q = *reinterpret_cast<const u32x2 *>(qrow + 8 * c);
+                const uint32_t q0w = q[0], q1w = q[1];
+                const u32x4 h0 = *reinterpret_cast<const u32x4 *>(hb + 16 * c);
+                const u32x4 h1 = *reinterpret_cast<const u32x4 *>(hb + 16 * c + 8);
+                if (FMT == 1) {
+                    const float p = dot8_fp4_bf16(q1w, h1, dot8_fp4_bf16(q0w, h0, 0.f));
+                    acc += p * e4m3_to_f32(sf[c]);
+                } else {
+                    const float p = dot8_int4_bf16(q1w, h1, dot8_int4_bf16(q0w, h0, 0.f));
+                    acc += p * bf2f(reinterpret_cast<const uint16_t *>(sf)[c >> 3]);
+                }
+            }
+        }
         acc = wave_sum(acc);
+        if (FMT == 1) acc *= *a.w.down.ts_shared;
         if (lane == 0) a.y[n0 + wave] = (uint16_t)f2bf(acc);
     }
 }
@@ -766,9 +794,12 @@ hipError_t launch_decode_chain(const Shape &s, const WSet *w, const float *const
 
 bool dense1_supported(const Shape &s, int fmt)
 {
-    return fmt == 0 && s.E == 0 && s.S == 1 && s.H % kG == 0 && s.H <= 2048 &&  // <= 8 down rows per workgroup
-           s.I % 8 == 0 && s.I >= 2 * kG && s.I <= kDenseMaxI &&              // 1..8 h words per workgroup
-           (size_t)(s.H / kG) * s.I * 2 <= 128 * 1024 && device_cus() >= kG;
+    const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + scale_row_bytes(fmt, s.I);
+    const int rows_h = s.H / kG;
+    return s.E == 0 && s.S == 1 && s.H % kG == 0 && s.H <= 2048 &&  // <= 8 down rows per workgroup
+           s.I % 128 == 0 && s.I >= 2 * kG && s.I <= kDenseMaxI &&  // 1..8 h words per workgroup
+           (size_t)rows_h * s.I / 2 % 16 == 0 && (size_t)rows_h * row % 16 == 0 &&  // whole chunks
+           (size_t)rows_h * row <= 128 * 1024 && device_cus() >= kG;
 }
 
 hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint16_t *y, void *head,
@@ -784,7 +815,11 @@ hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint1
     a.y = y;
     a.ctl = reinterpret_cast<uint32_t *>(hb);
     a.xh = reinterpret_cast<uint64_t *>(hb + kXHOff);
-    dense1_kernel<<<kG, 64 * kDenseWaves, (size_t)(s.H / kG) * s.I * 2, st>>>(a);
+    const size_t row = w.fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + scale_row_bytes(w.fmt, s.I);
+    const size_t dyn = (size_t)(s.H / kG) * row;
+    if (w.fmt == 0) dense1_kernel<0><<<kG, 64 * kDenseWaves, dyn, st>>>(a);
+    else if (w.fmt == 1) dense1_kernel<1><<<kG, 64 * kDenseWaves, dyn, st>>>(a);
+    else dense1_kernel<2><<<kG, 64 * kDenseWaves, dyn, st>>>(a);
     return hipGetLastError();
 }
 

@@ -254,6 +254,15 @@ def test_dense_single_token_shapes(H, I):
     _dense_check(1, H, I, fm.WFMT_BF16, layer=2)
 
 
+@pytest.mark.parametrize("fmt,H,I", [(fm.WFMT_NVFP4, 2048, 4096), (fm.WFMT_INT4, 2048, 4096),
+                                     (fm.WFMT_NVFP4, 512, 640), (fm.WFMT_INT4, 2048, 640),
+                                     (fm.WFMT_INT4, 1024, 2048)])
+def test_dense_single_token_4bit(fmt, H, I):
+    """The dense single-token launch with NVFP4 and INT4 weights: codes and scales of the
+    down rows staged in LDS, uneven h words per workgroup for I = 640."""
+    _dense_check(1, H, I, fmt, layer=4)
+
+
 def test_dense_and_moe_single_token_share_a_workspace():
     """The dense and the MoE single-token launches take turns on one workspace (the launch
     counter and the tagged words carry over from one to the other), through
