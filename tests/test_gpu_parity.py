@@ -259,8 +259,10 @@ def test_dense_single_token_shapes(H, I):
                                      (fm.WFMT_INT4, 1024, 2048)])
 def test_dense_single_token_4bit(fmt, H, I):
     """The dense single-token launch with NVFP4 and INT4 weights: codes and scales of the
-    down rows staged in LDS, uneven h words per workgroup for I = 640."""
+    down rows staged in LDS, uneven h words per workgroup for I = 640; through
+    flint_moe_layer and through flint_moe_forward."""
     _dense_check(1, H, I, fmt, layer=4)
+    _dense_check(1, H, I, fmt, layer=5, three_call=True)
 
 
 def test_dense_and_moe_single_token_share_a_workspace():
