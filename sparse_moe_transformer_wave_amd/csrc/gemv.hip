@@ -141,7 +141,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 #pragma unroll
         for (int mt = 0; mt < NMT; mt++) xr[mt] = x + (size_t)tix[mt] * H;
         const int nsc = H / 128;
-        constexpr int NB = 4;
+        // one super-chunk per wave and step: a wave holds only that step's codes and token
+        // fragments, so more workgroups fit on a CU (4 per step measured 8-10 % slower)
+        constexpr int NB = 1;
         for (int s0 = wave; s0 < nsc; s0 += 4 * NB) {
             u32x4 qv[RG][NB], a[NMT][NB][4];
             uint32_t sb[RG][NB];
@@ -315,7 +317,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
         const uint8_t *Sd = expert_sf(w.down, e, E, (size_t)H * srow) + (size_t)row * srow;
         if (FMT == 1) ts = expert_ts(w.down, e, E);
         const int nsc = I / 128, se = nsc * (kw + 1) / KS;
-        constexpr int NB = KS == 1 ? (NMT == 1 ? 6 : 3) : 2;
+        // split-K workgroups take one super-chunk per step (two measured 0.4-2.4 % slower)
+        constexpr int NB = KS == 1 ? (NMT == 1 ? 6 : 3) : 1;
         for (int s0 = nsc * kw / KS; s0 < se; s0 += NB) {
             u32x4 q[NB], a[NMT][NB][4];
             uint32_t sb[NB];
@@ -451,13 +454,14 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(int T, int H, int k, 
     *reinterpret_cast<u32x4 *>(y + (size_t)t * H + c) = outv;
 }
 
-// Gate/up, row groups per wave: 2 for bf16 and INT4 with one token tile, else 1 (NVFP4
-// dequantisation already keeps a wave busy: a second group measured slower).
+// Gate/up, row groups per wave: 2 with one token tile, else 1.  (With 4-bit weights taken
+// one super-chunk per step a wave needs few registers; a second NVFP4 group then measured
+// 3-5 % faster, four INT4 groups mixed: slower at T = 8, faster at T = 32.)
 template <int FMT, int NMT>
 static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, int cls, const uint16_t *x,
                           const int32_t *sa, const Plan &plan, uint16_t *h, hipStream_t st)
 {
-    constexpr int RG = FMT != 1 && NMT == 1 ? 2 : 1;
+    constexpr int RG = NMT == 1 ? 2 : 1;
     const unsigned grid = (unsigned)(maxU * (s.I / (8 * RG)));
     gemv_gateup_kernel<FMT, NMT, RG><<<grid, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, s.E == 0, w, x, sa,
                                                          plan, h);
