@@ -454,14 +454,21 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(int T, int H, int k, 
     *reinterpret_cast<u32x4 *>(y + (size_t)t * H + c) = outv;
 }
 
-// Gate/up, row groups per wave: 2 with one token tile, else 1.  (With 4-bit weights taken
-// one super-chunk per step a wave needs few registers; a second NVFP4 group then measured
-// 3-5 % faster, four INT4 groups mixed: slower at T = 8, faster at T = 32.)
+// Gate/up, row groups per wave: 2 with one token tile, else 1; 4-bit weights with more than
+// 16 tokens take 4.  (With 4-bit weights taken one super-chunk per step a wave needs few
+// registers: a second NVFP4 group measured 3-5 % faster; four groups measured slower at
+// T = 8 and 2-3 % faster at T = 32.)
 template <int FMT, int NMT>
 static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, int cls, const uint16_t *x,
                           const int32_t *sa, const Plan &plan, uint16_t *h, hipStream_t st)
 {
     constexpr int RG = NMT == 1 ? 2 : 1;
+    if (FMT != 0 && NMT == 1 && T > 16) {  // 4-bit, fuller units: four row groups
+        const unsigned grid4 = (unsigned)(maxU * (s.I / 32));
+        gemv_gateup_kernel<FMT, NMT, 4><<<grid4, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, s.E == 0, w, x, sa,
+                                                             plan, h);
+        return;
+    }
     const unsigned grid = (unsigned)(maxU * (s.I / (8 * RG)));
     gemv_gateup_kernel<FMT, NMT, RG><<<grid, 256, 0, st>>>((int)T, s.H, s.I, s.E, s.k, cls, s.E == 0, w, x, sa,
                                                          plan, h);
