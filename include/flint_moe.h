@@ -22,8 +22,11 @@
  *     Nothing throws across the ABI.
  *   - T == 0 is a no-op returning FLINT_OK once the descriptor is valid.
  *   - Supported shapes: 1 <= E <= 256; 1 <= k <= min(8, E); n_shared in {0, 1};
- *     hidden % 256 == 0 and 256 <= hidden <= 8192; inter % 128 == 0 and
- *     128 <= inter <= 4096; 0 <= T <= 65536.  Every pointer must be 16-byte aligned.
+ *     hidden % 64 == 0 and 64 <= hidden <= 8192; inter % 32 == 0 and
+ *     32 <= inter <= 4096; 0 <= T <= 65536.  INT4 weights also need hidden % 128 == 0 and
+ *     inter % 128 == 0 (a scale group is 128 columns).  Every pointer must be 16-byte
+ *     aligned.  (The inter % 32 granularity admits one GPU's share of a layer split over
+ *     inter, e.g. inter = 96 for 8 shares of 768.)
  *   - Dense layers: E == 0 with k == 0 and n_shared == 1 describes a dense SwiGLU FFN
  *     (the Flint model has 2 dense layers beside its 47 MoE layers: neoteo.com
  *     specification table, row "Warstwy"; their intermediate size is not given, so
@@ -34,9 +37,14 @@
  *     their scales must be NULL); flint_moe_route and flint_moe_permute return
  *     FLINT_ERR_SHAPE.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
- *   - A workspace's first 96 KiB hold the single-token path's launch counter, error flag
- *     and exchange words: zero them once before first use (flint_moe_workspace_init, or
- *     any zero fill) and leave them to the library afterwards.
+ *   - A workspace's first 96 KiB (the head) hold the persistent launches' ticket counter,
+ *     the error flags, the small-batch arrival counter and exchange words: zero them once
+ *     before first use (flint_moe_workspace_init, or any zero fill) and leave them to the
+ *     library afterwards.  Head words: u64 at byte 0 = ticket counter; u32 at byte 8 =
+ *     error flags (read and cleared by flint_moe_workspace_status); u32 at byte 12 = the
+ *     small-batch arrival counter; u32 at byte 16 = a diagnostic switch, 0 in normal use:
+ *     nonzero makes every bounded wait of the persistent launches give up at once (it
+ *     exists so that the timeout report can be tested; results are then unreliable).
  */
 #ifndef FLINT_MOE_H
 #define FLINT_MOE_H
@@ -57,6 +65,16 @@ enum {
     FLINT_ERR_WORKSPACE = 4,   /* ws_bytes < flint_moe_workspace_bytes(desc, T, format)  */
     FLINT_ERR_FORMAT = 5,      /* unknown weight format or missing scale arrays         */
     FLINT_ERR_HIP = 6          /* a kernel launch failed; see flint_moe_status_string    */
+};
+
+/* ---- workspace error flags (flint_moe_workspace_status) ---------------------------- */
+enum {
+    /* A bounded wait of a persistent launch (the single-token layer, the dense single-token
+       layer, every layer of a decode chain) ran out: its workgroups were not all resident
+       at once (another kernel held CUs), so that call's outputs are unreliable.  The
+       launch still ended normally, and later calls are unaffected: every launch's exchange
+       words carry a tag of their own. */
+    FLINT_WS_WAIT_TIMEOUT = 1
 };
 
 /* ---- weight formats ---------------------------------------------------------------- */
@@ -136,11 +154,19 @@ size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int3
    allocation).  Call once per workspace before its first use. */
 int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
+/* The error flags (FLINT_WS_*) that calls on this workspace have raised since the last
+   status call, written to *flags (a device int32, 4-byte aligned) by a one-thread kernel on
+   `stream`, which also clears them; queue it after the calls to check, and read *flags once
+   the stream has reached it.  0 = no error.  ws_bytes >= 96 KiB. */
+int flint_moe_workspace_status(void *ws, size_t ws_bytes, int32_t *flags, void *stream);
+
 /* Static text for a status code; for FLINT_ERR_HIP it also names the last HIP error
    seen by this library (the text is per thread and stays valid until the next call). */
 const char *flint_moe_status_string(int status);
 
-/* Router and selection.
+/* Router and selection: every token's router scores over the 256 routed experts and the
+   top 6 of them, weighted by sigmoid scores (recipes.vllm.ai "RecursiveSI/flint", Overview:
+   top-6 sigmoid routing; neoteo.com specification table, row "Eksperci": 6 of 256).
      logits[t][e] = sum_h x[t][h] * w_router[e][h] + (logit_bias ? logit_bias[e] : 0),
    accumulated in fp32 (x: bf16 [T][H]; w_router: fp32 [E][H]; logit_bias: fp32 [E]).
    topk_ids[t][0..k) = the k experts ordered by (logit descending, index ascending) on
@@ -153,18 +179,24 @@ int flint_moe_route(const flint_moe_desc *desc, int64_t T, const uint16_t *x,
                     int32_t *topk_ids, float *topk_w, uint32_t flags, void *ws,
                     size_t ws_bytes, void *stream);
 
-/* Grouping of the T*k assignments a = t*k + j by expert id:
-   counts[e] = #assignments of expert e; offsets = exclusive scan (offsets[E] = T*k);
+/* Grouping of the T*k assignments a = t*k + j by expert id, the data movement in front of
+   a fused MoE expert kernel (recipes.vllm.ai "RecursiveSI/flint", Overview, the fused MoE
+   kernel): counts[e] = #assignments of expert e; offsets = exclusive scan (offsets[E] = T*k);
    sorted_assign = assignments grouped by expert, ascending a inside a group;
    assign_pos[a] = position of a in sorted_assign.  Integer, bit-exact.
-   Ids outside [0, E) are a caller error: their assignments are dropped.
+   Ids outside [0, E) are a caller error: such an assignment is dropped (in no count, its
+   assign_pos is -1, and sorted_assign holds -1 from offsets[E] on); flint_moe_forward then
+   leaves it out of the combine.
    ws may be NULL; given flint_moe_workspace_bytes(desc, T, ...) bytes, large T
    (T*k > 4096) uses a faster multi-block grouping with the same result. */
 int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk_ids,
                       int32_t *counts, int32_t *offsets, int32_t *sorted_assign,
                       int32_t *assign_pos, void *ws, size_t ws_bytes, void *stream);
 
-/* Experts and combine:
+/* Experts and combine: the selected experts and the always-active shared expert, each a
+   SwiGLU FFN, summed with the routing weights (news.ditty.ir, third paragraph, and
+   neoteo.com specification table, row "Eksperci": 6 routed experts plus one shared expert
+   that is always active; the SwiGLU form and the weight-one shared expert are readings):
      y[t] = bf16( o_shared(t) + sum_j topk_w[t][j] * o_{topk_ids[t][j]}(t) ),
      o_e(t) = down_e( silu(gate_e x_t) * (up_e x_t) ),
    summed in fp32 in that order (shared first, then j ascending), which makes y
@@ -172,7 +204,8 @@ int flint_moe_permute(const flint_moe_desc *desc, int64_t T, const int32_t *topk
    grouped-GEMM path (T > 32) each per-slot output o is also rounded to bf16 before the
    combine, while the streaming path (T <= 32) combines o in fp32.
    topk_ids/topk_w/offsets/sorted_assign/assign_pos are the outputs of route and
-   permute for the same T.  y: bf16 [T][H].
+   permute for the same T (an assignment whose assign_pos is outside [0, T*k) is left out
+   of the sum).  y: bf16 [T][H].
    A dense layer (n_experts == 0) with one token, 512 <= I <= 4096 and H <= 2048 (any
    weight format) runs as one persistent launch that exchanges h through the workspace
    head, like flint_moe_layer's single-token launch below (same device and head
@@ -183,16 +216,18 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
                       const int32_t *assign_pos, uint16_t *y, void *ws, size_t ws_bytes,
                       void *stream);
 
-/* The whole layer: route (x, w_router, logit_bias), permute and forward, with the same
-   results as the three calls above.  `routing` (may be NULL) receives the intermediate
+/* The whole layer (the MoE FFN layer of the pages above: router, top-6 of 256 routed
+   experts, shared expert, combine): route (x, w_router, logit_bias), permute and forward,
+   with the same results as the three calls above.  `routing` (may be NULL) receives the intermediate
    routing tensors the caller asks for.  A single token (T == 1) runs as one persistent
    launch of one workgroup per CU (on a device with at least 256 CUs) whose workgroups
    exchange logits and h through tagged words at the start of the workspace (see
    flint_moe_workspace_init); it rounds h to bf16 like the other paths and combines the
    per-slot outputs in fp32; a dense layer's single bf16 token likewise (see
-   flint_moe_forward).  A wait there
-   that runs out (it cannot on a device with a CU per workgroup) sets the word at byte 4
-   of the workspace to 1. */
+   flint_moe_forward).  These launches need all 256 workgroups resident at once; they are
+   chosen only on a device with at least 256 CUs where one workgroup fits on a CU.  A wait
+   there that runs out (other work holding CUs) raises FLINT_WS_WAIT_TIMEOUT in the
+   workspace (flint_moe_workspace_status). */
 int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
                     const uint16_t *x, const float *w_router, const float *logit_bias,
                     uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,
@@ -224,8 +259,10 @@ enum {
    kernel registers that its single-layer form keeps for loads in flight.)
    layers: host array [n_layers] (read during the call only).  All layers share `desc` and
    one weight format.  x: bf16 [H]; y: bf16 [n_layers][H], every layer's output y_l;
-   topk_ids / topk_w: [n_layers][k] or NULL; logits: [n_layers][E] fp32 or NULL.  Needs the single-token persistent path:
-   E >= 1, hidden <= 2048, inter <= 1024, k <= 8, and a device with at least 256 CUs
+   topk_ids / topk_w: [n_layers][k] or NULL; logits: [n_layers][E] fp32 or NULL.  Needs the
+   single-token persistent path: E >= 1, hidden % 256 == 0 and hidden <= 2048,
+   inter <= 1024, k <= 8, the down rows of one 1/256 slice of hidden in whole 16-byte
+   chunks, and a device with at least 256 CUs where one workgroup fits on a CU
    (FLINT_ERR_SHAPE otherwise).  ws: at least flint_moe_workspace_bytes(desc, 1, format)
    bytes, initialised once (flint_moe_workspace_init).  0 <= n_layers <= 4096. */
 int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref *layers,

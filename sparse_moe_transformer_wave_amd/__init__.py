@@ -6,7 +6,8 @@ kernels behind the C ABI (include/flint_moe.h).  There is no fallback: if the na
 library is missing, every call raises.
 
 Entry points (same names as the C ABI, without the prefix):
-  workspace_bytes(desc, T_max, fmt), workspace_init(ws), workspace(desc, T_max, fmt)
+  workspace_bytes(desc, T_max, fmt), workspace_init(ws), workspace(desc, T_max, fmt),
+  workspace_status(ws) (error flags raised since the last status call, then cleared)
   route(desc, x, w_router, bias, topk_ids, topk_w, ws, logits=None, logits_in=False)
   permute(desc, topk_ids, counts, offsets, sorted_assign, assign_pos, ws)
   forward(desc, weights, x, topk_ids, topk_w, offsets, sorted_assign, assign_pos, y, ws)
@@ -25,8 +26,12 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_FORMAT, ERR_HIP = range(7
 WFMT_BF16, WFMT_NVFP4, WFMT_INT4 = 0, 1, 2
 ROUTE_LOGITS_IN = 1
 CHAIN_RESIDUAL = 1
+WS_WAIT_TIMEOUT = 1
+# byte offsets of the workspace head's words (include/flint_moe.h)
+HEAD_TICKET, HEAD_ERROR, HEAD_ARRIVALS, HEAD_DIAG = 0, 8, 12, 16
 
-EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_workspace_init", "flint_moe_status_string",
+EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_workspace_init", "flint_moe_workspace_status",
+            "flint_moe_status_string",
             "flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer",
             "flint_moe_decode_chain")
 
@@ -76,6 +81,8 @@ def lib():
         L.flint_moe_workspace_bytes.restype = sz
         L.flint_moe_workspace_init.argtypes = [vp, sz, vp]
         L.flint_moe_workspace_init.restype = ctypes.c_int
+        L.flint_moe_workspace_status.argtypes = [vp, sz, vp, vp]
+        L.flint_moe_workspace_status.restype = ctypes.c_int
         L.flint_moe_status_string.argtypes = [ctypes.c_int]
         L.flint_moe_status_string.restype = ctypes.c_char_p
         L.flint_moe_route.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp]
@@ -160,6 +167,16 @@ def workspace_init(ws, stream=None):
     """Zero the synchronisation words of a workspace tensor (once, before first use)."""
     _check(lib().flint_moe_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)),
            "flint_moe_workspace_init")
+
+
+def workspace_status(ws, stream=None) -> int:
+    """Error flags (WS_*) raised on this workspace since the last status call, then cleared.
+    Queues the status kernel on the stream and waits for it (this helper synchronises)."""
+    import torch
+    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    _check(lib().flint_moe_workspace_status(_ptr(ws), _nbytes(ws), _ptr(out), _stream(stream)),
+           "flint_moe_workspace_status")
+    return int(out.item())
 
 
 def workspace(d: Desc, T_max: int, fmt: int = WFMT_BF16):

@@ -30,8 +30,8 @@ int check_desc(const flint_moe_desc *d)
         if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts) return FLINT_ERR_SHAPE;
         if (d->n_shared != 0 && d->n_shared != 1) return FLINT_ERR_SHAPE;
     }
-    if (d->hidden < 256 || d->hidden > 8192 || d->hidden % 256) return FLINT_ERR_SHAPE;
-    if (d->inter < 128 || d->inter > 4096 || d->inter % 128) return FLINT_ERR_SHAPE;
+    if (d->hidden < 64 || d->hidden > 8192 || d->hidden % 64) return FLINT_ERR_SHAPE;
+    if (d->inter < 32 || d->inter > 4096 || d->inter % 32) return FLINT_ERR_SHAPE;
     if (d->renormalize != 0 && d->renormalize != 1) return FLINT_ERR_SHAPE;
     return FLINT_OK;
 }
@@ -48,11 +48,18 @@ int hip_status(hipError_t e)
     return FLINT_ERR_HIP;
 }
 
+// INT4 scale groups are 128 columns of K (H for gate/up, I for down).
+bool format_fits(const flint_moe_desc *d, int32_t format)
+{
+    return format != FLINT_WFMT_INT4 || (d->hidden % 128 == 0 && d->inter % 128 == 0);
+}
+
 int check_weights(const flint_moe_desc *d, const flint_moe_weights *w)
 {
     if (!w) return FLINT_ERR_NULL;
     if (w->format != FLINT_WFMT_BF16 && w->format != FLINT_WFMT_NVFP4 && w->format != FLINT_WFMT_INT4)
         return FLINT_ERR_FORMAT;
+    if (!format_fits(d, w->format)) return FLINT_ERR_SHAPE;
     const bool dense = d->n_experts == 0;
     if (dense) {  // no routed experts: their pointers must be NULL
         const void *rp[] = {w->gate, w->up, w->down, w->gate_sf, w->up_sf, w->down_sf,
@@ -193,7 +200,16 @@ size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int3
 {
     if (check_desc(desc) != FLINT_OK || T_max < 0 || T_max > kMaxT) return 0;
     if (format != FLINT_WFMT_BF16 && format != FLINT_WFMT_NVFP4 && format != FLINT_WFMT_INT4) return 0;
+    if (!format_fits(desc, format)) return 0;
     return ws_layout(shape_of(desc), T_max).total;
+}
+
+int flint_moe_workspace_status(void *ws, size_t ws_bytes, int32_t *flags, void *stream)
+{
+    if (!ws || !flags) return FLINT_ERR_NULL;
+    if (!aligned16(ws) || ((uintptr_t)flags & 3u)) return FLINT_ERR_ALIGN;
+    if (ws_bytes < kSyncBytes) return FLINT_ERR_WORKSPACE;
+    return hip_status(launch_ws_status(ws, flags, (hipStream_t)stream));
 }
 
 const char *flint_moe_status_string(int status)
@@ -363,7 +379,7 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     }
     if (T <= kGemvMaxT) {
         rc = hip_status(launch_router_select(s, T, x, w_router, logit_bias, lg, ids, tw, cnt, off,
-                                             sa, ap, plan, (int *)(b + L.sync) + 2, st));
+                                             sa, ap, plan, (int *)(b + L.sync + kHeadArrivals), st));
         if (rc) return rc;
     } else {
         rc = hip_status(launch_router(s, T, x, w_router, logit_bias, lg, st));

@@ -96,10 +96,29 @@ hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, co
                                 const float *bias, float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap,
                                 const Plan &plan, int *arrivals, hipStream_t st);
-// Single-token layer in one persistent launch (decode1.hip).  `head` = the workspace's
-// first kSyncBytes (launch counter and exchange words; zero before first use).
-// decode1_supported also checks that the current device has a CU for every workgroup.
+// Workspace head: the first kSyncBytes of every workspace (zeroed once before first use).
+//   u64 at kHeadTicket    ticket counter: every workgroup of a persistent launch takes one
+//                         ticket (each such launch has exactly kPersistentGrid workgroups),
+//                         so ticket / kPersistentGrid numbers the launch and gives its tag
+//   u32 at kHeadError     error flags (FLINT_WS_WAIT_TIMEOUT); cleared by the status call
+//   u32 at kHeadArrivals  arrival counter of the small-batch router launch (re-armed by it)
+//   u32 at kHeadDiag      diagnostic switch: nonzero makes every bounded wait give up at once
+//   exchange words of the persistent launches from kHeadXchg on
 constexpr size_t kSyncBytes = 96 * 1024;
+constexpr size_t kHeadTicket = 0, kHeadError = 8, kHeadArrivals = 12, kHeadDiag = 16, kHeadXchg = 1024;
+constexpr int kPersistentGrid = 256;
+constexpr uint32_t kWsWaitTimeout = 1u;  // FLINT_WS_WAIT_TIMEOUT
+// Tag of a persistent launch from one of its tickets: 1 .. 2^32 - 1, never 0 (the value of a
+// zeroed exchange word), and different for consecutive launches.
+__host__ __device__ inline uint32_t launch_tag(uint64_t ticket)
+{
+    return (uint32_t)((ticket / kPersistentGrid) % 0xffffffffull) + 1u;
+}
+// Copies the head's error flags to *out and clears them (one thread).
+hipError_t launch_ws_status(void *head, int32_t *out, hipStream_t st);
+// Single-token layer in one persistent launch (decode1.hip).  `head` = the workspace head.
+// decode1_supported also checks that the current device has a CU for every workgroup and
+// that one workgroup of the launch fits on a CU (registers and LDS).
 bool decode1_supported(const Shape &s, int fmt);
 hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, const float *Wr,
                           const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
@@ -162,15 +181,16 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c)
 }
 
 // Eight E2M1 nibbles (one 32-bit word, low nibble first) times a block scale, as 8 bf16
-// (4 words).  gfx950's FP4 conversion applies only the power-of-two part of its scale
-// operand, so it yields e2m1 * 2^floor(log2 scale) exactly; one fp32 multiply by the
-// remaining mantissa factor (1 + m/8 for an E4M3 scale) completes the product.  A 2-bit
-// times a 4-bit significand is exact in fp32 and in bf16, so keeping the upper halves
-// (v_perm_b32) is exact.  A zero scale gives zeros.
+// (4 words).  gfx950's FP4 conversion applies only the exponent of its scale operand (its
+// sign too is ignored: a sweep over every finite E4M3 scale showed negative scales coming
+// back positive), so it yields e2m1 * 2^floor(log2 |scale|) exactly; one fp32 multiply by
+// the remaining signed mantissa factor (+-(1 + m/8) for an E4M3 scale) completes the
+// product.  A 2-bit times a 4-bit significand is exact in fp32 and in bf16, so keeping the
+// upper halves (v_perm_b32) is exact.  A zero scale gives zeros.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 dequant8(uint32_t q, float scale)
 {
-    const float mant = __uint_as_float((__float_as_uint(scale) & 0x007fffffu) | 0x3f800000u);
+    const float mant = __uint_as_float((__float_as_uint(scale) & 0x807fffffu) | 0x3f800000u);
     const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 0);
     const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 1);
     const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 2);

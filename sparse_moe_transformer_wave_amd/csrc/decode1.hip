@@ -27,13 +27,20 @@
 // written with agent-scope stores and polled with agent-scope loads: one aligned 64-bit
 // access carries the payload and its readiness together, so there are no grid barriers,
 // fences or cache-wide write-backs, and a reader waits one round trip after the word it
-// needs lands.  The tag is the launch counter at the start of the workspace plus one;
-// workgroup 0 advances the counter once it has seen every workgroup's phase-1 word (each
-// was written after its writer read the counter), and the next launch on the stream
-// starts after this one ends.  Every wait is bounded: on timeout the kernel sets an error
-// word and carries on.  All 256 workgroups must be resident together (one per CU); the
-// host checks the CU count before choosing this launch.
+// needs lands.  Each workgroup takes one ticket from the workspace head's ticket counter
+// when it starts; a launch has exactly 256 workgroups, so the 256 tickets of one launch
+// share ticket / 256, which gives the launch its tag.  A workgroup that starts late still
+// takes a ticket of its own launch (the next launch on the stream starts after every
+// workgroup of this one has ended), so a word it publishes never carries a later launch's
+// tag.  Every wait is bounded: on timeout the kernel sets the head's error flag (read and
+// cleared by flint_moe_workspace_status) and carries on with the values it has.  All 256
+// workgroups must be resident together (one per CU): the host checks the CU count and the
+// kernel's occupancy before choosing this launch.
 #include "common.h"
+
+#include <map>
+#include <mutex>
+#include <tuple>
 
 namespace flint {
 
@@ -45,18 +52,29 @@ constexpr int kMaxK = 8;
 constexpr int kMaxXC = 4;      // 16-byte x chunks per lane: H <= 2048
 constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
 
-// Workspace words of this launch (the zero-initialised head of the workspace):
-// u32 [0] launch counter, u32 [1] error flag; u64 exchange words for the logits at byte
-// 1024 (one per workgroup: the fp32 logit) and for h at byte 3072 ([(k + S + 1) / 2][I]:
-// word (q, i) holds bf16 h of slots 2 q (low half) and 2 q + 1 (high half) at row i; slot
-// k = shared expert).  Every workgroup reads all of h, so two values per word halve the
-// polling traffic, and h is rounded to bf16 before the down rows on every path anyway.
-// A chain of layers hands each token to the next launch through the bf16 [2048] buffer at
-// kXNextOff.
-constexpr int kCtlEpoch = 0, kCtlError = 1;
-constexpr size_t kXLogOff = 1024, kXHOff = kXLogOff + 8 * kG;
+// Exchange words in the workspace head (see common.h for the head's control words): u64
+// words for the logits at kXLogOff (one per workgroup: the fp32 logit) and for h at kXHOff
+// ([(k + S + 1) / 2][I]: word (q, i) holds bf16 h of slots 2 q (low half) and 2 q + 1 (high
+// half) at row i; slot k = shared expert).  Every workgroup reads all of h, so two values per
+// word halve the polling traffic, and h is rounded to bf16 before the down rows on every path
+// anyway.  A chain of layers hands each token to the next launch through the bf16 [2048]
+// buffer at kXNextOff.
+constexpr size_t kXLogOff = kHeadXchg, kXHOff = kXLogOff + 8 * kG;
 constexpr size_t kXNextOff = kXHOff + 8 * (size_t)(kMaxK + 1) * 1024;
 static_assert(kXNextOff + 2 * 2048 <= kSyncBytes, "exchange words exceed the head");
+static_assert(kG == kPersistentGrid, "one ticket per workgroup of a persistent launch");
+
+// Ticket of this workgroup (one thread asks; the caller broadcasts the tag it gives).
+__device__ __forceinline__ uint64_t take_ticket(uint8_t *head)
+{
+    return __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(head + kHeadTicket), 1ull, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t diag_word(const uint8_t *head)
+{
+    return __hip_atomic_load(reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(head) + kHeadDiag),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -85,18 +103,20 @@ __device__ __forceinline__ uint64_t get_word(const uint64_t *p)
 
 // Waits until the words w[q] (q < nq, read from p + stride * q) all carry `tag`.  The
 // missing ones are re-read together, so each try costs one round trip however many are
-// late.  Bounded: on timeout the error flag is set and the stale values are kept.
+// late.  Bounded: on timeout (at once when `giveup`, the head's diagnostic switch) the error
+// flag is set and the stale values are kept.
 template <int N>
 __device__ __forceinline__ void await_words(const uint64_t *p, int stride, int nq, uint64_t *w, uint32_t tag,
-                                            uint32_t *ctl)
+                                            uint8_t *head, bool giveup)
 {
     for (int n = 0;; n++) {
         bool miss = false;
 #pragma unroll
         for (int q = 0; q < N; q++) miss |= q < nq && (uint32_t)(w[q] >> 32) != tag;
         if (!miss) break;
-        if (n >= kSpin) {
-            __hip_atomic_store(ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (giveup || n >= kSpin) {
+            __hip_atomic_fetch_or(reinterpret_cast<uint32_t *>(head + kHeadError), kWsWaitTimeout, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -197,7 +217,7 @@ struct D1Args {
     int32_t *ids;
     float *tw;
     int32_t *counts, *offsets, *sa, *ap;  // null in a chain
-    uint32_t *ctl;   // launch counter, error flag
+    uint8_t *head;   // workspace head: ticket counter, error flags, diagnostic switch
     uint64_t *xlog;  // [256] exchange words: logit of expert b (workgroup b)
     uint64_t *xh;    // [(k + S + 1) / 2][I] exchange words, two slots each: slot j < k = j-th
                      // selected expert, slot k = shared
@@ -269,6 +289,7 @@ struct D1Shared {
     float wt[kMaxK];
     float dts[kMaxK + 1];         // NVFP4 down tensor scale of every slot
     float o[kMaxK + 1][8];        // per-slot down outputs of this workgroup's rows_h columns
+    uint32_t tag, giveup;         // this launch's tag and the diagnostic switch (from wave 0)
     __attribute__((aligned(16))) uint16_t hb[(kMaxK + 1) * 1024];  // h of every slot, bf16 [slot][I]
 };
 
@@ -283,7 +304,14 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     const int rows_h = H / kG;                        // down rows (columns of y) per workgroup
     const int n0 = b * rows_h;
     const int i0 = b * I / kG, npair = (b + 1) * I / kG - i0;  // gate/up rows of every expert
-    const uint32_t tag = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // The ticket is asked for before anything else; wave 0 needs its tag only once its router
+    // row is in (its loads return in order), the other waves read it from LDS after phase 1.
+    uint64_t ticket = 0;
+    uint32_t diag = 0;
+    if (tid == 0) {
+        ticket = take_ticket(a.head);
+        diag = diag_word(a.head);
+    }
     const size_t drow_bytes = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2 + scale_row_bytes(FMT, I);
     const int cpb = (int)(rows_h * drow_bytes / 16);  // 16-byte chunks per slot block
     const int ngrp = (cpb + 63) / 64;                 // 64-chunk groups per slot block
@@ -348,6 +376,11 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         if (S) load_down(k, E, 0, kWaves);
     }
     if (wave == 0) {
+        const uint32_t tag0 = __builtin_amdgcn_readlane(launch_tag(ticket), 0);
+        if (lane == 0) {
+            sh.tag = tag0;
+            sh.giveup = diag;
+        }
         const int e = b;
         if (e < E) {      // router row: one logit
             float acc = 0.f;
@@ -362,10 +395,10 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
             const float l = wave_sum(acc) + (a.bias ? a.bias[e] : 0.f);
             if (lane == 0) {
                 if (a.logits) a.logits[e] = l;
-                put_word(a.xlog + b, tag, l);
+                put_word(a.xlog + b, tag0, l);
             }
         } else if (lane == 0) {
-            put_word(a.xlog + b, tag, 0.f);  // no expert: the word only says "counter read"
+            put_word(a.xlog + b, tag0, 0.f);  // no expert: the word only says "workgroup started"
         }
     } else if (S) {
         // shared expert rows r = 2 (i - i0) + {0 gate, 1 up}, r < 2 npair: wave 1 + r % 7
@@ -383,6 +416,8 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         }
     }
     __syncthreads();
+    const uint32_t tag = sh.tag;
+    const bool giveup = sh.giveup != 0;
     // the shared slot k has a word of its own when k is even; otherwise it shares one with
     // slot k - 1 and goes out in phase 2
     if (S && (k & 1) == 0 && tid < npair)
@@ -393,11 +428,9 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         uint64_t lw[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) lw[i] = get_word(a.xlog + lane + 64 * i);
-        await_words<4>(a.xlog + lane, 64, 4, lw, tag, a.ctl);
+        await_words<4>(a.xlog + lane, 64, 4, lw, tag, a.head, giveup);
 #pragma unroll
         for (int i = 0; i < 4; i++) sh.lg[lane + 64 * i] = __uint_as_float((uint32_t)lw[i]);
-        // every workgroup has read the counter: the next launch may use the next tag
-        if (b == 0 && lane == 0) __hip_atomic_store(a.ctl + kCtlEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     // Lane holds experts lane + 64 i.  Key = order of the logit (select_key's high word)
@@ -527,7 +560,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         uint64_t hw[NH];
 #pragma unroll
         for (int q = 0; q < NH; q++) hw[q] = q < nq ? get_word(a.xh + tid + kPollT * q) : 0ull;
-        await_words<NH>(a.xh + tid, kPollT, nq, hw, tag, a.ctl);
+        await_words<NH>(a.xh + tid, kPollT, nq, hw, tag, a.head, giveup);
 #pragma unroll
         for (int q = 0; q < NH; q++) {
             if (q < nq) {
@@ -607,8 +640,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 //               the rows' codes, then their scales), and take no part in polling (a
 //               wave's loads return in order).
 //   all         down row n = wave of the slice against h from LDS -> y.
-// The launch counter advances once workgroup 0 has seen every word: each was written
-// after its writer read the counter, so every workgroup has read it.
+// The launch tag comes from the workgroup's ticket, as in decode1_kernel.
 constexpr int kDenseRowWaves = 8, kDenseWaves = kDenseRowWaves + 4, kDenseMaxI = 4096;
 
 template <int FMT>
@@ -616,6 +648,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];  // down rows of the slice
     __shared__ __attribute__((aligned(16))) uint16_t hb[kDenseMaxI];
+    __shared__ uint32_t s_tag[2];  // this launch's tag, the diagnostic switch
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, b = blockIdx.x;
     const int H = a.H, I = a.I, W = I / 2;
     const int rows_h = H / kG, n0 = b * rows_h;
@@ -626,6 +659,12 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
     // for no load, so the gate/up rows, on which h and the exchange wait, are ahead of the
     // down rows in the memory queues and the down rows land while h is exchanged.
     const bool rows = wave < kDenseRowWaves && wave < nq;
+    uint64_t ticket = 0;  // asked for first; needed only once the rows' products are done
+    uint32_t diag = 0;
+    if (tid == 0) {
+        ticket = take_ticket(a.head);
+        diag = diag_word(a.head);
+    }
     const int i = 2 * (q0 + wave);
     RowLoad<FMT> rl[4];  // gate i, up i, gate i + 1, up i + 1
     u32x4 xb[kMaxXC];
@@ -653,10 +692,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // read after the row loads, whose data the dots wait for anyway (a wave's loads return
-    // in order), so that nothing before the barrier waits for a load
-    const uint32_t tag = wave < kDenseRowWaves
-        ? __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 0u;
+    float d[4];
     if (wave >= kDenseRowWaves) {
         const size_t drow = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2;  // code (or bf16) bytes per row
         const int ncq = (int)(rows_h * drow / 16);                      // 16-byte chunks of them
@@ -668,24 +704,34 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
             if (c < cpb) lds_load16(c < ncq ? src + 16 * c : ssrc + 16 * (c - ncq), dyn + (size_t)64 * g * 16);
         }
     } else if (rows) {
-        float d[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) d[r] = row_dot<FMT>(a, rl[r], xb, xf);
-        if (lane == 0) put_h2(a.xh + q0 + wave, tag, silu(d[0]) * d[1], silu(d[2]) * d[3]);
     }
+    // The tag reaches every wave through LDS behind a barrier that waits for LDS writes
+    // only (the copy waves' copies stay in flight).
+    if (tid == 0) {
+        s_tag[0] = launch_tag(ticket);
+        s_tag[1] = diag;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const uint32_t tag = s_tag[0];
+    const bool giveup = s_tag[1] != 0;
+    if (rows && lane == 0) put_h2(a.xh + q0 + wave, tag, silu(d[0]) * d[1], silu(d[2]) * d[3]);
     if (wave < kDenseRowWaves) {
         constexpr int kPollT = 64 * kDenseRowWaves, NH = kDenseMaxI / 2 / kPollT;
         const int nw = tid < W ? (W - tid + kPollT - 1) / kPollT : 0;
         uint64_t hw[NH];
 #pragma unroll
         for (int q = 0; q < NH; q++) hw[q] = q < nw ? get_word(a.xh + tid + kPollT * q) : 0ull;
-        await_words<NH>(a.xh + tid, kPollT, nw, hw, tag, a.ctl);
+        await_words<NH>(a.xh + tid, kPollT, nw, hw, tag, a.head, giveup);
 #pragma unroll
         for (int q = 0; q < NH; q++)
             if (q < nw) reinterpret_cast<uint32_t *>(hb)[tid + kPollT * q] = (uint32_t)hw[q];
     }
     __syncthreads();  // h in LDS; the copy waves' down rows have landed
-    if (b == 0 && tid == 0) __hip_atomic_store(a.ctl + kCtlEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (wave < rows_h) {
         float acc = 0.f;
         if (FMT == 0) {
@@ -726,18 +772,35 @@ static size_t d1_dyn_bytes(const Shape &s, int fmt)
     return (size_t)(s.k + s.S) * (s.H / kG) * row;
 }
 
-// CU count of the current device, asked once per device.
-static int device_cus()
+// A persistent launch needs every one of its kG workgroups resident at once: a device with
+// at least kG CUs, and room on a CU for one workgroup of the kernel (registers and LDS,
+// hipOccupancyMaxActiveBlocksPerMultiprocessor).  Asked once per (device, kernel, LDS bytes).
+// It cannot see other work on the GPU: a launch that shares the CUs with other kernels may
+// find its waits running out, which the workspace's error flags report.
+static bool persistent_fits(const void *kernel, int threads, size_t dyn)
 {
-    static int cus[64];
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void *, size_t>, bool> known;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cus[dev] = n;
-    }
-    return cus[dev];
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    const auto key = std::make_tuple(dev, kernel, dyn);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = known.find(key);
+    if (it != known.end()) return it->second;
+    int cus = 0, blocks = 0;
+    const bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                    cus >= kG &&
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, dyn) == hipSuccess &&
+                    blocks >= 1;
+    known[key] = ok;
+    return ok;
+}
+
+static const void *decode1_entry(int fmt)
+{
+    return fmt == 0 ? reinterpret_cast<const void *>(&decode1_kernel<0>)
+         : fmt == 1 ? reinterpret_cast<const void *>(&decode1_kernel<1>)
+                    : reinterpret_cast<const void *>(&decode1_kernel<2>);
 }
 
 bool decode1_supported(const Shape &s, int fmt)
@@ -747,7 +810,8 @@ bool decode1_supported(const Shape &s, int fmt)
     return s.E >= 1 && s.H % kG == 0 && s.H <= 2048 &&                   // rows_h <= 8, x in 4 chunks per lane
            s.I % 32 == 0 && s.I <= 1024 && s.k <= kMaxK &&    // <= 4 gate/up pairs: one row per wave
            (size_t)rows_h * row % 16 == 0 &&                  // whole 16-byte chunks per block
-           d1_dyn_bytes(s, fmt) + sizeof(D1Shared) <= 160 * 1024 && device_cus() >= kG;
+           d1_dyn_bytes(s, fmt) + sizeof(D1Shared) <= 160 * 1024 &&
+           persistent_fits(decode1_entry(fmt), 512, d1_dyn_bytes(s, fmt));
 }
 
 static hipError_t launch_d1(const Shape &s, int fmt, const D1Args &a, hipStream_t st)
@@ -767,7 +831,7 @@ hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, cons
 {
     char *hb = static_cast<char *>(head);
     D1Args a{s.H, s.I, s.E, s.k, s.S, s.renorm, w, x, Wr, bias, y, nullptr, 0, logits, ids, tw,
-             counts, offsets, sa, ap, reinterpret_cast<uint32_t *>(hb),
+             counts, offsets, sa, ap, reinterpret_cast<uint8_t *>(hb),
              reinterpret_cast<uint64_t *>(hb + kXLogOff), reinterpret_cast<uint64_t *>(hb + kXHOff)};
     return launch_d1(s, w.fmt, a, st);
 }
@@ -784,7 +848,7 @@ hipError_t launch_decode_chain(const Shape &s, const WSet *w, const float *const
                  y + (size_t)l * s.H, l + 1 < L || hand_on ? xnext : nullptr, residual ? 1 : 0,
                  logits ? logits + (size_t)l * s.E : nullptr, ids ? ids + (size_t)l * s.k : nullptr,
                  tw ? tw + (size_t)l * s.k : nullptr, nullptr, nullptr, nullptr, nullptr,
-                 reinterpret_cast<uint32_t *>(hb), reinterpret_cast<uint64_t *>(hb + kXLogOff),
+                 reinterpret_cast<uint8_t *>(hb), reinterpret_cast<uint64_t *>(hb + kXLogOff),
                  reinterpret_cast<uint64_t *>(hb + kXHOff)};
         const hipError_t e = launch_d1(s, w[l].fmt, a, st);
         if (e != hipSuccess) return e;
@@ -796,10 +860,13 @@ bool dense1_supported(const Shape &s, int fmt)
 {
     const size_t row = fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + scale_row_bytes(fmt, s.I);
     const int rows_h = s.H / kG;
+    const void *entry = fmt == 0 ? reinterpret_cast<const void *>(&dense1_kernel<0>)
+                      : fmt == 1 ? reinterpret_cast<const void *>(&dense1_kernel<1>)
+                                 : reinterpret_cast<const void *>(&dense1_kernel<2>);
     return s.E == 0 && s.S == 1 && s.H % kG == 0 && s.H <= 2048 &&  // <= 8 down rows per workgroup
            s.I % 128 == 0 && s.I >= 2 * kG && s.I <= kDenseMaxI &&  // 1..8 h words per workgroup
            (size_t)rows_h * s.I / 2 % 16 == 0 && (size_t)rows_h * row % 16 == 0 &&  // whole chunks
-           (size_t)rows_h * row <= 128 * 1024 && device_cus() >= kG;
+           (size_t)rows_h * row <= 128 * 1024 && persistent_fits(entry, 64 * kDenseWaves, (size_t)rows_h * row);
 }
 
 hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint16_t *y, void *head,
@@ -813,13 +880,28 @@ hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint1
     a.w = w;
     a.x = x;
     a.y = y;
-    a.ctl = reinterpret_cast<uint32_t *>(hb);
+    a.head = reinterpret_cast<uint8_t *>(hb);
     a.xh = reinterpret_cast<uint64_t *>(hb + kXHOff);
     const size_t row = w.fmt == 0 ? (size_t)s.I * 2 : (size_t)s.I / 2 + scale_row_bytes(w.fmt, s.I);
     const size_t dyn = (size_t)(s.H / kG) * row;
     if (w.fmt == 0) dense1_kernel<0><<<kG, 64 * kDenseWaves, dyn, st>>>(a);
     else if (w.fmt == 1) dense1_kernel<1><<<kG, 64 * kDenseWaves, dyn, st>>>(a);
     else dense1_kernel<2><<<kG, 64 * kDenseWaves, dyn, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace flint
+
+namespace flint {
+
+__global__ void ws_status_kernel(uint32_t *flags, int32_t *out)
+{
+    *out = (int32_t)__hip_atomic_exchange(flags, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_ws_status(void *head, int32_t *out, hipStream_t st)
+{
+    ws_status_kernel<<<1, 1, 0, st>>>(reinterpret_cast<uint32_t *>(static_cast<char *>(head) + kHeadError), out);
     return hipGetLastError();
 }
 

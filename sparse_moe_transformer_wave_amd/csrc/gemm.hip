@@ -3,15 +3,19 @@
 // Prefill is compute-heavy rather than weight-bound (recipes.vllm.ai "RecursiveSI/flint",
 // Benchmarking: the NVFP4 checkpoint barely changes the 8K-token prefill time), so the
 // expert FFNs run on bf16 MFMA with fp32 accumulation and LDS-staged tiles: bf16 weights
-// through a ring of K stages filled HBM -> LDS directly (gemm_bf16_kernel), NVFP4 weights
-// and INT4 weights through registers, where they are dequantised, with a prefetch of the
-// next K step (grouped_gemm_kernel).
+// through a ring of K stages filled HBM -> LDS directly (gemm_bf16_kernel); 4-bit weights as
+// their codes through a register ring, dequantised once into a bf16 LDS stage
+// (gemm_q4_kernel, K a multiple of 128); NVFP4 weights whose K is not a multiple of 128
+// through registers into a padded double buffer, dequantised on the way, with a prefetch of
+// the next K step and zeros past K (grouped_gemm_kernel).
 //
 // Work items come from the device plan: one item = (touched expert, 256-row tile of its
-// slots), so an expert of up to 256 rows streams its weights once.  Gate/up: A = the expert's tokens gathered from x, B = 32 gate rows and the same
-// 32 up rows per wave column, epilogue h = bf16(silu(g) * u).  Down: A = h rows of the
-// expert's slots (contiguous), epilogue o = bf16(acc).  The combine then forms
-// y = o_shared + sum_j w_j o_j per token, in that fixed order.
+// slots), so an expert of up to 256 rows streams its weights once.  Gate/up: A = the
+// expert's tokens gathered from x, B = gate rows and the same up rows per wave column,
+// epilogue h = bf16(silu(g) * u).  Down: A = h rows of the expert's slots (contiguous),
+// epilogue o = bf16(acc).  N tiles past the matrix (I not a multiple of 128 for gate/up, H
+// not a multiple of 256 for down) read a repeat of the last row and store nothing.  The
+// combine then forms y = o_shared + sum_j w_j o_j per token, in that fixed order.
 #include "common.h"
 
 namespace flint {
@@ -38,7 +42,10 @@ __device__ __forceinline__ void xcd_map(int b, int n_tiles, int &item, int &nb)
     item = x + kXcds * (q / n_tiles);
 }
 
-template <int MODE, int FMT>
+// NVFP4 weights with K not a multiple of 128 (K a multiple of 16): the same 256 x 256 tiles
+// and work items as the kernels below, A and B staged through registers into a padded
+// double buffer, 64-wide K steps, the next step's loads in flight while the MFMAs run.
+template <int MODE>
 __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, int E, int k,
                                                           WSet w,
                                                           const uint16_t *__restrict__ asrc,
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
     const int N = MODE == 0 ? 2 * I : H;  // B rows of the whole problem
-    const int n_tiles = N / BN;
+    const int n_tiles = (N + BN - 1) / BN;
     int item, nb;
     xcd_map(blockIdx.x, n_tiles, item, nb);
     if (item >= p.meta[1]) return;
@@ -83,40 +90,29 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
         if (MODE == 0) {
             const int wcol = rr >> 6, within = rr & 63;
             mat = (within >> 5) ? &w.up : &w.gate;
-            n = nb * (BN / 2) + wcol * 32 + (within & 31);
+            n = min(nb * (BN / 2) + wcol * 32 + (within & 31), I - 1);
         } else {
             mat = &w.down;
-            n = nb * BN + rr;
+            n = min(nb * BN + rr, H - 1);
         }
-        if (FMT == 0) {
-            const size_t mb = (size_t)H * I * 2;
-            brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * K * 2;
-            bsf[j] = nullptr;
-        } else {
-            const size_t mb = (size_t)H * I / 2, srow = scale_row_bytes(FMT, K), sb = (size_t)(H * I / K) * srow;
-            brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2);
-            bsf[j] = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * srow;
-        }
+        const size_t mb = (size_t)H * I / 2, srow = scale_row_bytes(1, K), sb = (size_t)(H * I / K) * srow;
+        brow[j] = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2);
+        bsf[j] = (sh ? mat->sf_shared : mat->sf_routed + (size_t)e * sb) + (size_t)n * srow;
     }
     const int schunk = tid & 7;
 
     u32x4 ra[NP], rb[NP];
-    auto gload = [&](int k0) {
+    auto gload = [&](int k0) {  // columns past K (the last stage when K % 64 != 0) are zeros
+        const int kk = k0 + schunk * 8;
+        const bool in = kk < K;
 #pragma unroll
         for (int j = 0; j < NP; j++) {
-            ra[j] = ld16g(arow[j] + k0 + schunk * 8);
-            if (FMT == 0) {
-                rb[j] = ld16g(brow[j] + (size_t)(k0 + schunk * 8) * 2);
-            } else {
-                const int kk = k0 + schunk * 8;
-                uint32_t q = *reinterpret_cast<const uint32_t *>(brow[j] + kk / 2);
-                if (FMT == 1) {
-                    rb[j] = dequant8(q, e4m3_to_f32(bsf[j][kk / 16]));
-                } else {
-                    const float s = bf2f(reinterpret_cast<const uint16_t *>(bsf[j])[kk / 128]);
-                    rb[j] = dequant8_int4(q, s);
-                }
-            }
+            ra[j] = u32x4{0u, 0u, 0u, 0u};
+            rb[j] = u32x4{0u, 0u, 0u, 0u};
+            if (!in) continue;
+            ra[j] = ld16g(arow[j] + kk);
+            const uint32_t q = *reinterpret_cast<const uint32_t *>(brow[j] + kk / 2);
+            rb[j] = dequant8(q, e4m3_to_f32(bsf[j][kk / 16]));
         }
     };
     auto lstore = [&](int buf) {
@@ -134,7 +130,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
+    const int nk = (K + BK - 1) / BK;
     gload(0);
     lstore(0);
     __syncthreads();
@@ -160,12 +156,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
     }
 
     // Epilogue.  acc[ms][ns][i] = D[row = wm*64 + ms*16 + 4g + i][brow = wn*64 + ns*16 + r].
-    float tsg = 1.f, tsu = 1.f, tsd = 1.f;
-    if (FMT == 1) {
-        tsg = sh ? *w.gate.ts_shared : w.gate.ts_routed[e];
-        tsu = sh ? *w.up.ts_shared : w.up.ts_routed[e];
-        tsd = sh ? *w.down.ts_shared : w.down.ts_routed[e];
-    }
+    const float tsg = sh ? *w.gate.ts_shared : w.gate.ts_routed[e];
+    const float tsu = sh ? *w.up.ts_shared : w.up.ts_routed[e];
+    const float tsd = sh ? *w.down.ts_shared : w.down.ts_routed[e];
 #pragma unroll
     for (int ms = 0; ms < 4; ms++) {
 #pragma unroll
@@ -178,13 +171,13 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
                 for (int ns = 0; ns < 2; ns++) {
                     const int col = nb * (BN / 2) + wn * 32 + ns * 16 + r;
                     const float gv = acc[ms][ns][i] * tsg, uv = acc[ms][ns + 2][i] * tsu;
-                    out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
+                    if (col < I) out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
                 }
             } else {
 #pragma unroll
                 for (int ns = 0; ns < 4; ns++) {
                     const int col = nb * BN + wn * 64 + ns * 16 + r;
-                    out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i] * tsd);
+                    if (col < H) out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i] * tsd);
                 }
             }
         }
@@ -221,7 +214,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
     constexpr int kRow = 64, kTile = 256 * kRow, kStage = 2 * kTile;  // bytes
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];     // NS * kStage
     const int N = MODE == 0 ? 2 * I : H;
-    const int n_tiles = N / BN;
+    const int n_tiles = (N + BN - 1) / BN;
     int item, nb;
     xcd_map(blockIdx.x, n_tiles, item, nb);
     if (item >= p.meta[1]) return;
@@ -254,10 +247,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
         if (MODE == 0) {  // each 64-row wave column: 32 gate rows, then the same 32 up rows
             const int wcol = crow >> 6, within = crow & 63;
             mat = (within >> 5) ? &w.up : &w.gate;
-            n = nb * (BN / 2) + wcol * 32 + (within & 31);
+            n = min(nb * (BN / 2) + wcol * 32 + (within & 31), I - 1);
         } else {
             mat = &w.down;
-            n = nb * BN + crow;
+            n = min(nb * BN + crow, H - 1);
         }
         const size_t mb = (size_t)H * I;
         bp_ = reinterpret_cast<const uint16_t *>(sh ? mat->shared : mat->routed) + (sh ? 0 : (size_t)e * mb) +
@@ -322,13 +315,13 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
 #pragma unroll
                 for (int ns = 0; ns < 2; ns++) {
                     const int col = nb * (BN / 2) + wn * 32 + ns * 16 + r;
-                    out[slot * I + col] = (uint16_t)f2bf(silu(acc[ms][ns][i]) * acc[ms][ns + 2][i]);
+                    if (col < I) out[slot * I + col] = (uint16_t)f2bf(silu(acc[ms][ns][i]) * acc[ms][ns + 2][i]);
                 }
             } else {
 #pragma unroll
                 for (int ns = 0; ns < 4; ns++) {
                     const int col = nb * BN + wn * 64 + ns * 16 + r;
-                    out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i]);
+                    if (col < H) out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i]);
                 }
             }
         }
@@ -361,7 +354,7 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // NSA A stages + 2 B stages
     uint8_t *const bbuf = lds + NSA * kStage;
     const int N = MODE == 0 ? 2 * I : H;
-    const int n_tiles = N / BN;
+    const int n_tiles = (N + BN - 1) / BN;
     int item, nb;
     xcd_map(blockIdx.x, n_tiles, item, nb);
     if (item >= p.meta[1]) return;
@@ -409,10 +402,10 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
         if (MODE == 0) {
             const int wcol = bro >> 7, within = bro & 127;
             mat = (within >> 6) ? &w.up : &w.gate;
-            n = nb * (BN / 2) + wcol * 64 + (within & 63);
+            n = min(nb * (BN / 2) + wcol * 64 + (within & 63), I - 1);
         } else {
             mat = &w.down;
-            n = nb * BN + bro;
+            n = min(nb * BN + bro, H - 1);
         }
         const size_t mb = (size_t)H * I / 2, srow = scale_row_bytes(FMT, K), sb = (size_t)(H * I / K) * srow;
         qp = (sh ? mat->shared : mat->routed + (size_t)e * mb) + (size_t)n * (K / 2) + 8 * hq;
@@ -521,13 +514,13 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
                 for (int ns = 0; ns < 4; ns++) {
                     const int col = nb * (BN / 2) + wn * 64 + ns * 16 + r;
                     const float gv = acc[ms][ns][i] * tsg, uv = acc[ms][ns + 4][i] * tsu;
-                    out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
+                    if (col < I) out[slot * I + col] = (uint16_t)f2bf(silu(gv) * uv);
                 }
             } else {
 #pragma unroll
                 for (int ns = 0; ns < 8; ns++) {
                     const int col = nb * BN + wn * 128 + ns * 16 + r;
-                    out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i] * tsd);
+                    if (col < H) out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i] * tsd);
                 }
             }
         }
@@ -535,6 +528,7 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
 }
 
 // y[t][n] = bf16(o[T*k + t][n] + sum_j w[t][j] * o[ap[t*k + j]][n]); 8 columns per thread.
+// Slots outside [0, T k) (assignments dropped for an out-of-range expert id) are skipped.
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int S,
                                                       const uint16_t *__restrict__ o,
                                                       const float *__restrict__ topk_w,
@@ -558,8 +552,10 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int S
         for (int i = 0; i < 8; i++) acc[i] = 0.f;
     }
     for (int j = 0; j < k; j++) {
+        const int sl = ap[t * k + j];
+        if (sl < 0 || sl >= T * k) continue;  // a dropped assignment (expert id out of range) has no slot
         const float wj = topk_w[t * k + j];
-        u32x4 v = ld16g(o + (size_t)ap[t * k + j] * H + c);
+        u32x4 v = ld16g(o + (size_t)sl * H + c);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             acc[2 * i] += wj * bf2f(v[i] & 0xffffu);
@@ -582,26 +578,26 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
     const int64_t slots = T * s.k + T * s.S;
     const int64_t max_items = (slots + kGemmBM - 1) / kGemmBM + s.E + s.S;
     const int64_t item_slots = (max_items + kXcds - 1) / kXcds * kXcds;
-    const unsigned g1 = (unsigned)(item_slots * (2 * s.I / BN));
-    const unsigned g2 = (unsigned)(item_slots * (s.H / BN));
+    const unsigned g1 = (unsigned)(item_slots * ((2 * s.I + BN - 1) / BN));
+    const unsigned g2 = (unsigned)(item_slots * ((s.H + BN - 1) / BN));
     if (w.fmt == 0) {
         constexpr size_t lds = (size_t)kRingStages * 2 * 256 * 64;
         gemm_bf16_kernel<0, kRingStages><<<g1, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
         gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     } else {
-        // 4-bit weights: the code ring needs K in whole trips of four 32-wide stages
+        // 4-bit weights: the code ring needs K in whole trips of four 32-wide stages (INT4
+        // always has them: its scale groups are 128 columns); NVFP4 with K % 128 != 0 takes
+        // the register-staged kernel
         constexpr size_t qlds = (size_t)(5 + 2) * 256 * 64;
         const bool ring_gu = s.H % 128 == 0, ring_dn = s.I % 128 == 0;
         if (w.fmt == 1) {
             if (ring_gu) gemm_q4_kernel<0, 1><<<g1, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-            else grouped_gemm_kernel<0, 1><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+            else grouped_gemm_kernel<0><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
             if (ring_dn) gemm_q4_kernel<1, 1><<<g2, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
-            else grouped_gemm_kernel<1, 1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+            else grouped_gemm_kernel<1><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
         } else {
-            if (ring_gu) gemm_q4_kernel<0, 2><<<g1, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-            else grouped_gemm_kernel<0, 2><<<g1, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-            if (ring_dn) gemm_q4_kernel<1, 2><<<g2, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
-            else grouped_gemm_kernel<1, 2><<<g2, NT, 0, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+            gemm_q4_kernel<0, 2><<<g1, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+            gemm_q4_kernel<1, 2><<<g2, NTQ, qlds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
         }
     }
     const int64_t nthreads = T * (s.H / 8);

@@ -4,6 +4,8 @@
 // The grouping is the data movement a fused MoE kernel needs (recipes.vllm.ai
 // "RecursiveSI/flint", Overview, "fused MoE"): counts, exclusive offsets, the stable
 // order (ascending assignment index inside each expert) and its inverse.  All integer.
+// An assignment whose id lies outside [0, E) is dropped: it is in no count, its
+// assign_pos is -1, and sorted_assign holds -1 past offsets[E] (every path below).
 #include "common.h"
 
 namespace flint {
@@ -114,11 +116,13 @@ __device__ void group_by_expert(int n, int E, const int32_t *ids, GroupScratch &
         g.cursor[e] = g.off[e];
     }
     if (tid == 0) offsets[E] = g.off[E];
+    for (int p = g.off[E] + tid; p < n; p += 1024) sa[p] = -1;  // past the valid assignments
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base = 0; base < n; base += 1024) {
         const int a = base + tid;
         int e = (a < n) ? ids[a] : -1;
         const bool valid = (e >= 0 && e < E);
+        if (!valid && a < n) ap[a] = -1;
         for (int i = tid; i < 16 * 256; i += 1024) (&g.wave_cnt[0][0])[i] = 0;
         __syncthreads();
         uint64_t peers = __ballot(valid);
@@ -208,7 +212,10 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
         const int pos = g.off[e] + before;
         sa[pos] = tid;
         ap[tid] = pos;
+    } else if (tid < n) {
+        ap[tid] = -1;
     }
+    if (tid >= g.off[E] && tid < n) sa[tid] = -1;
     // units of at most kUnitRows rows (as in build_plan's streaming case)
     const int nf = E + S;
     if (tid < nf) {
@@ -319,7 +326,8 @@ __global__ __launch_bounds__(1024) void perm_hist_kernel(int n, int E, const int
 __global__ __launch_bounds__(256) void perm_scan_kernel(int T, int E, int k, int S, int H, int nb,
                                                         int32_t *__restrict__ hist,
                                                         int32_t *__restrict__ counts,
-                                                        int32_t *__restrict__ offsets, Plan plan,
+                                                        int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ sa, Plan plan,
                                                         int with_plan)
 {
     __shared__ int cnt[256];
@@ -359,6 +367,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int T, int E, int k, int
         }
     }
     if (e == 0) offsets[E] = off[E];
+    for (int p = off[E] + (int)threadIdx.x; p < T * k; p += 256) sa[p] = -1;  // past the valid assignments
     if (with_plan) build_plan(T, E, k, S, H, cnt, off, plan, ps);
 }
 
@@ -391,6 +400,8 @@ __global__ __launch_bounds__(1024) void perm_scatter_kernel(int n, int E, const 
         const int pos = base[(size_t)blockIdx.x * E + e] + before + rank;
         sa[pos] = a;
         ap[a] = pos;
+    } else if (a < n) {
+        ap[a] = -1;
     }
 }
 
@@ -409,7 +420,7 @@ hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t
     }
     const int nb = (n + 1023) / 1024;
     perm_hist_kernel<<<nb, 1024, 0, st>>>(n, s.E, ids, hist);
-    perm_scan_kernel<<<1, 256, 0, st>>>((int)T, s.E, s.k, s.S, s.H, nb, hist, counts, offsets, p,
+    perm_scan_kernel<<<1, 256, 0, st>>>((int)T, s.E, s.k, s.S, s.H, nb, hist, counts, offsets, sa, p,
                                         plan ? 1 : 0);
     perm_scatter_kernel<<<nb, 1024, 0, st>>>(n, s.E, ids, hist, sa, ap);
     return hipGetLastError();

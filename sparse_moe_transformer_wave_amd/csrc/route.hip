@@ -127,10 +127,10 @@ __global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
     // Iteration kt: stage kt in LDS buffer kt % 2, stage kt + 1 in flight in registers
     // (issued two iterations ago), stage kt + 2 issued now into the registers freed by the
     // previous iteration's store.
-    const int nk = H / RBK;  // >= 4
+    const int nk = H / RBK;  // >= 1 (H is a multiple of 64)
     RouterStage s0, s1;
     gload(0, s0);
-    gload(RBK, s1);
+    if (nk > 1) gload(RBK, s1);
     lstore(0, s0);
     __syncthreads();
     auto step = [&](int kt, RouterStage &nxt, RouterStage &fill) {
@@ -140,8 +140,8 @@ __global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
         __syncthreads();
     };
     for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, s1, s0);      // stage kt + 1 sits in s1; s0 (stored) takes stage kt + 2
-        step(kt + 1, s0, s1);  // stage kt + 2 sits in s0; s1 takes stage kt + 3
+        step(kt, s1, s0);                      // stage kt + 1 sits in s1; s0 (stored) takes stage kt + 2
+        if (kt + 1 < nk) step(kt + 1, s0, s1);  // stage kt + 2 sits in s0; s1 takes stage kt + 3
     }
     // acc[ms][i] = logit of token t0 + wt*64 + ms*16 + 4g + i, expert e0 + we*16 + r
     const int e = e0 + we * 16 + r;

@@ -189,3 +189,30 @@ def test_int4_weight_validation():
     d0 = fm.desc(2048, 768, n_shared=0)
     sh_sf_without_shared = fm.Weights(fm.WFMT_INT4, A, A, A, None, None, None, A, A, A, A, None, None)
     assert _forward(d0, sh_sf_without_shared.c_struct(), 8, nb=need) == fm.ERR_FORMAT
+
+
+def test_shape_contract_h64_i32():
+    """hidden % 64 and inter % 32 (bf16, NVFP4); INT4 also needs hidden % 128 and inter % 128
+    (its scale groups are 128 columns)."""
+    for H, I in ((64, 32), (320, 96), (2048, 96), (192, 160), (8192, 4096)):
+        d = fm.desc(H, I)
+        assert fm.workspace_bytes(d, 8, fm.WFMT_BF16) > 0
+        assert fm.workspace_bytes(d, 8, fm.WFMT_NVFP4) > 0
+        assert (fm.workspace_bytes(d, 8, fm.WFMT_INT4) > 0) == (H % 128 == 0 and I % 128 == 0)
+    for H, I in ((32, 32), (96, 32), (2048, 16), (2048, 48), (8256, 32), (2048, 4128)):
+        assert fm.workspace_bytes(fm.desc(H, I), 8) == 0, (H, I)
+    d = fm.desc(2048, 96)
+    need = fm.workspace_bytes(d, 8, fm.WFMT_NVFP4)
+    int4 = fm.Weights(fm.WFMT_INT4, A, A, A, A, A, A, A, A, A, A, A, A)
+    assert _forward(d, int4.c_struct(), 8, nb=need) == fm.ERR_SHAPE
+    assert _forward(fm.desc(384, 128), int4.c_struct(), 8, nb=fm.workspace_bytes(fm.desc(384, 128), 8, 2) - 1) \
+        == fm.ERR_WORKSPACE
+
+
+def test_workspace_status_validation():
+    L = fm.lib()
+    assert L.flint_moe_workspace_status(None, 1 << 20, A, None) == fm.ERR_NULL
+    assert L.flint_moe_workspace_status(A, 1 << 20, None, None) == fm.ERR_NULL
+    assert L.flint_moe_workspace_status(MIS, 1 << 20, A, None) == fm.ERR_ALIGN
+    assert L.flint_moe_workspace_status(A, 1 << 20, A + 2, None) == fm.ERR_ALIGN
+    assert L.flint_moe_workspace_status(A, 1024, A, None) == fm.ERR_WORKSPACE

@@ -21,12 +21,39 @@ def _say(msg):
     print(msg, flush=True)
 
 
+def _tickets(ws):
+    """The workspace head's ticket counter: every workgroup of a persistent launch (256 of
+    them) takes one ticket."""
+    return int(ws[fm.HEAD_TICKET:fm.HEAD_TICKET + 8].view(torch.int64).item())
+
+
+def _tile_edge_tokens(c, g, n_hot=4, bm=256):
+    """Tokens in the first and the last row of every 256-row tile of the n_hot experts with
+    the most rows and of the shared expert (slot T k + t holds token t), from the GPU's own
+    grouping."""
+    counts, off, sa = g["counts"], g["offsets"], g["sorted_assign"]
+    toks = set()
+    for e in np.argsort(-counts, kind="stable")[:n_hot]:
+        n = int(counts[e])
+        for m0 in range(0, n, bm):
+            for r in (m0, min(m0 + bm, n) - 1):
+                toks.add(int(sa[off[e] + r]) // c.k)
+    for m0 in range(0, c.T, bm):
+        toks.update((m0, min(m0 + bm, c.T) - 1))
+    return np.array(sorted(toks), np.int64)
+
+
 def _parity(c, steps=False, tokens=None):
+    """tokens: None (all), an index array, or a function of the GPU's host-side outputs
+    returning one (for samples chosen from the GPU's own grouping)."""
     _say("case T=%d H=%d I=%d E=%d k=%d S=%d fmt=%d" % (c.T, c.H, c.I, c.E, c.k, c.S, c.fmt))
     c.upload()
     g = c.run_steps() if steps else c.run_layer()
     rep = {}
     w64 = check_routing(c, g, rep)
+    if callable(tokens):
+        tokens = tokens(g)
+        _say("  %d sampled tokens" % len(tokens))
     rm, rl = check_forward(c, g, w64, tokens)
     _say("  ok: max rel %.2e, rel L1 %.2e, near ties %s" % (rm, rl, rep.get("near_ties")))
     return g
@@ -157,17 +184,21 @@ def test_full_decode_nvfp4(T):
 
 @pytest.mark.parametrize("zipf", [False, True])
 def test_full_prefill_8192(zipf):
+    """Routing on all 8192 tokens; y on a spread of tokens plus, from the GPU's grouping,
+    the tokens in the first and last row of every 256-row tile of the four experts with the
+    most rows (under the Zipf bias, the hot experts with up to ~18 tiles) and of the shared
+    expert (32 tiles)."""
     c = _full_case(8192, bias_c=dg.ZIPF_C if zipf else None)
-    toks = np.unique(np.concatenate([np.arange(0, 8192, 523), [8191]])).astype(np.int64)
-    _parity(c, tokens=toks)
+    spread = np.unique(np.concatenate([np.arange(0, 8192, 523), [8191]])).astype(np.int64)
+    _parity(c, tokens=lambda g: np.union1d(spread, _tile_edge_tokens(c, g)))
 
 
 @pytest.mark.parametrize("fmt", [fm.WFMT_BF16, fm.WFMT_NVFP4])
 def test_single_token_launch_reuses_workspace(fmt):
     """T = 1 runs as one persistent launch whose workgroups exchange logits and h through
     launch-tagged words at the start of the workspace: consecutive calls on one workspace
-    (each reading words the previous call tagged) all match the reference, the launch
-    counter advances by one per call and no wait ever timed out."""
+    (each reading words the previous call tagged) all match the reference, the ticket
+    counter advances by 256 per call (one per workgroup) and no wait ever timed out."""
     d = fm.desc(2048, 768)
     ws = fm.workspace(d, 1, fmt)
     for n_call, layer in enumerate((0, 1, 2, 3, 0)):
@@ -181,9 +212,8 @@ def test_single_token_launch_reuses_workspace(fmt):
         g = to_host(out, c)
         w64 = check_routing(c, g)
         rm, rl = check_forward(c, g, w64)
-        head = ws[:8].view(torch.int32).cpu().numpy()
-        assert head[1] == 0, "a wait timed out"
-        assert head[0] == n_call + 1, head
+        assert fm.workspace_status(ws) == 0, "a wait timed out"
+        assert _tickets(ws) == 256 * (n_call + 1)
         _say("layer %d fmt %d: max rel %.2e rel L1 %.2e" % (layer, fmt, rm, rl))
 
 
@@ -285,7 +315,7 @@ def test_dense_and_moe_single_token_share_a_workspace():
         g = to_host(out, c)
         w64 = check_routing(c, g, {})
         check_forward(c, g, w64, None)
-    assert int(ws[4:8].view(torch.int32).item()) == 0  # no wait ran out
+    assert fm.workspace_status(ws) == 0  # no wait ran out
 
 
 def test_dense_full_prefill_8192():
@@ -341,9 +371,8 @@ def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
         rm, rl = check_forward(c, g, w64)
         _say("  layer %d: max rel %.2e, rel L1 %.2e" % (l, rm, rl))
         xl = _next_token(xl, yg[l:l + 1], residual)
-    head = ws[:8].view(torch.int32).cpu().numpy()
-    assert head[1] == 0, "a wait timed out"
-    return ws, head
+    assert fm.workspace_status(ws) == 0, "a wait timed out"
+    return ws, _tickets(ws)
 
 
 @pytest.mark.parametrize("residual", [False, True])
@@ -356,10 +385,10 @@ def test_chain_tiny(residual):
 
 def test_chain_tiny_two_launches_and_counter():
     """20 layers (the host gathers layer descriptors 16 at a time, so the token crosses
-    that boundary too); the launch counter advances once per layer, and a following
+    that boundary too); the ticket counter advances by 256 per layer, and a following
     single-token layer call on the same workspace is still correct."""
-    ws, head = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 20, True)
-    assert head[0] == 20, head
+    ws, tickets = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 20, True)
+    assert tickets == 20 * 256, tickets
     c = Case(1, 256, 128, 256, 6, layer=3).upload()
     out = c.alloc_out()
     routing = {kk: out[kk] for kk in ("logits", "topk_ids", "topk_w", "counts", "offsets",
@@ -369,8 +398,7 @@ def test_chain_tiny_two_launches_and_counter():
     from moe_cases import to_host
     g = to_host(out, c)
     check_forward(c, g, check_routing(c, g))
-    head = ws[:8].view(torch.int32).cpu().numpy()
-    assert head[0] == 21 and head[1] == 0, head
+    assert _tickets(ws) == 21 * 256 and fm.workspace_status(ws) == 0
 
 
 def test_chain_tiny_nvfp4():
@@ -449,5 +477,4 @@ def test_graph_replays_match_eager(T):
         torch.cuda.synchronize()
         assert torch.equal(y_eager, ref)
     if T == 1:
-        head = ws[:8].view(torch.int32).cpu().numpy()
-        assert head[1] == 0, "a wait timed out"
+        assert fm.workspace_status(ws) == 0, "a wait timed out"
