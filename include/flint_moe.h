@@ -233,6 +233,21 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
                     uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+   harnesses that forbid hipMalloc): flint_moe_layer without a workspace argument.  Its
+   workspace is a 16 MiB array in device memory that the library holds on every GPU it runs
+   on until the process ends (zero when the library is loaded there); the call allocates
+   nothing.  Every call on one GPU shares that GPU's array, so calls that overlap on one GPU
+   (other streams, other threads) race: order them, e.g. on one stream.  The array's head is
+   the workspace head described above, never cleared by a call; its error flags are not
+   reported (use flint_moe_layer with a workspace of your own to read them).
+   Returns FLINT_ERR_WORKSPACE when flint_moe_workspace_bytes(desc, T, format) exceeds
+   16 MiB (at H = 2048, I = 768, E = 256, k = 6 with a shared expert: T above about 200);
+   otherwise exactly as flint_moe_layer. */
+int flint_moe_layer_noalloc(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
+                            const uint16_t *x, const float *w_router, const float *logit_bias,
+                            uint16_t *y, const flint_moe_routing *routing, void *stream);
+
 /* ---- persistent decode across layers ---------------------------------------------- */
 /* One MoE layer of a chain: its expert weights, router weights [E][H] fp32 and optional
    logit bias [E] (device pointers, checked like flint_moe_layer's). */

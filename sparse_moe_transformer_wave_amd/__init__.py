@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, without the prefix):
   permute(desc, topk_ids, counts, offsets, sorted_assign, assign_pos, ws)
   forward(desc, weights, x, topk_ids, topk_w, offsets, sorted_assign, assign_pos, y, ws)
   layer(desc, weights, x, w_router, bias, y, ws, routing=None)
+  layer_noalloc(desc, weights, x, w_router, bias, y, routing=None) (no workspace argument)
+  decode_chain(desc, layers, x, y, ws, ...)
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ HEAD_TICKET, HEAD_ERROR, HEAD_ARRIVALS, HEAD_DIAG = 0, 8, 12, 16
 EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_workspace_init", "flint_moe_workspace_status",
             "flint_moe_status_string",
             "flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer",
-            "flint_moe_decode_chain")
+            "flint_moe_decode_chain", "flint_moe_layer_noalloc")
 
 
 class FlintError(RuntimeError):
@@ -89,10 +91,11 @@ def lib():
         L.flint_moe_permute.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.flint_moe_forward.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.flint_moe_layer.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.flint_moe_layer_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp]
         L.flint_moe_decode_chain.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_uint32, vp, vp, vp, vp,
                                              vp, vp, sz, vp]
         for f in ("flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer",
-                  "flint_moe_decode_chain"):
+                  "flint_moe_decode_chain", "flint_moe_layer_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -224,6 +227,19 @@ def layer(d: Desc, weights: Weights, T: int, x, w_router, bias, y, ws, routing: 
                                _ptr(bias), _ptr(y), None if r is None else ctypes.byref(r),
                                _ptr(ws), _nbytes(ws), _stream(stream))
     _check(rc, "flint_moe_layer")
+
+
+def layer_noalloc(d: Desc, weights: Weights, T: int, x, w_router, bias, y, routing: dict | None = None,
+                  stream=None):
+    """flint_moe_layer_noalloc: the whole layer on the library's own per-GPU scratch array."""
+    w = weights.c_struct()
+    r = None
+    if routing:
+        r = _Routing(**{k: _ptr(v) for k, v in routing.items()})
+    rc = lib().flint_moe_layer_noalloc(ctypes.byref(d), ctypes.byref(w), T, _ptr(x), _ptr(w_router),
+                                       _ptr(bias), _ptr(y), None if r is None else ctypes.byref(r),
+                                       _stream(stream))
+    _check(rc, "flint_moe_layer_noalloc")
 
 
 def layer_refs(layers):

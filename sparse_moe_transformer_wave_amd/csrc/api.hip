@@ -4,6 +4,7 @@
 #include "../../include/flint_moe.h"
 #include "common.h"
 
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -129,6 +130,36 @@ WSet wset_of(const flint_moe_weights *w)
     s.up = mk(w->up, w->sh_up, w->up_sf, w->sh_up_sf, w->up_ts, 1);
     s.down = mk(w->down, w->sh_down, w->down_sf, w->sh_down_sf, w->down_ts, 2);
     return s;
+}
+
+}  // namespace
+
+// Workspace of flint_moe_layer_noalloc: one copy per GPU, zero when the library's code object
+// is loaded on that device and kept for the life of the process.  Host code never uses this
+// name as an address: it asks hipGetSymbolAddress for the device's copy (noalloc_scratch).
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+
+// Device address of the current device's `scratch`, looked up once per device.
+int noalloc_scratch(void **out)
+{
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= 64) return hip_status(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (es != hipSuccess) return hip_status(es);
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return FLINT_OK;
 }
 
 }  // namespace
@@ -329,10 +360,12 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
                         plan, st);
 }
 
-int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
-                    const uint16_t *x, const float *w_router, const float *logit_bias,
-                    uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,
-                    void *stream)
+}  // extern "C"
+
+// Arguments of flint_moe_layer other than the workspace; T == 0 passes (a no-op).
+static int check_layer_args(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
+                            const uint16_t *x, const float *w_router, const float *logit_bias,
+                            const uint16_t *y, const flint_moe_routing *routing)
 {
     int rc = check_desc(desc);
     if (rc) return rc;
@@ -341,16 +374,33 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
     if (rc) return rc;
     if (T == 0) return FLINT_OK;
     const bool dense = desc->n_experts == 0;  // no router: w_router, logit_bias, routing unused
-    if (!x || (!dense && !w_router) || !y || !ws) return FLINT_ERR_NULL;
-    const void *ptrs[] = {x, w_router, logit_bias, y, ws};
+    if (!x || (!dense && !w_router) || !y) return FLINT_ERR_NULL;
+    const void *ptrs[] = {x, w_router, logit_bias, y};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FLINT_ERR_ALIGN;
+    if (routing) {
+        const void *rptrs[] = {routing->logits, routing->topk_ids, routing->topk_w, routing->counts,
+                               routing->offsets, routing->sorted_assign, routing->assign_pos};
+        for (const void *p : rptrs)
+            if (!aligned16(p)) return FLINT_ERR_ALIGN;
+    }
+    return FLINT_OK;
+}
+
+extern "C" {
+
+int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
+                    const uint16_t *x, const float *w_router, const float *logit_bias,
+                    uint16_t *y, const flint_moe_routing *routing, void *ws, size_t ws_bytes,
+                    void *stream)
+{
+    int rc = check_layer_args(desc, weights, T, x, w_router, logit_bias, y, routing);
+    if (rc || T == 0) return rc;
+    if (!ws) return FLINT_ERR_NULL;
+    if (!aligned16(ws)) return FLINT_ERR_ALIGN;
+    const bool dense = desc->n_experts == 0;
     flint_moe_routing R{};
     if (routing) R = *routing;
-    const void *rptrs[] = {R.logits, R.topk_ids, R.topk_w, R.counts, R.offsets, R.sorted_assign,
-                           R.assign_pos};
-    for (const void *p : rptrs)
-        if (!aligned16(p)) return FLINT_ERR_ALIGN;
     const Shape s = shape_of(desc);
     const WsLayout L = ws_layout(s, T);
     if (ws_bytes < L.total) return FLINT_ERR_WORKSPACE;
@@ -436,6 +486,20 @@ int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref
         if (rc) return rc;
     }
     return FLINT_OK;
+}
+
+int flint_moe_layer_noalloc(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
+                            const uint16_t *x, const float *w_router, const float *logit_bias,
+                            uint16_t *y, const flint_moe_routing *routing, void *stream)
+{
+    int rc = check_layer_args(desc, weights, T, x, w_router, logit_bias, y, routing);
+    if (rc || T == 0) return rc;
+    if (ws_layout(shape_of(desc), T).total > kNoallocScratchBytes) return FLINT_ERR_WORKSPACE;
+    void *ws = nullptr;
+    rc = noalloc_scratch(&ws);
+    if (rc) return rc;
+    return flint_moe_layer(desc, weights, T, x, w_router, logit_bias, y, routing, ws, kNoallocScratchBytes,
+                           stream);
 }
 
 }  // extern "C"

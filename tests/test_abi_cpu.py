@@ -216,3 +216,21 @@ def test_workspace_status_validation():
     assert L.flint_moe_workspace_status(MIS, 1 << 20, A, None) == fm.ERR_ALIGN
     assert L.flint_moe_workspace_status(A, 1 << 20, A + 2, None) == fm.ERR_ALIGN
     assert L.flint_moe_workspace_status(A, 1024, A, None) == fm.ERR_WORKSPACE
+
+
+def test_layer_noalloc_validation():
+    """flint_moe_layer_noalloc validates like flint_moe_layer, and rejects a T whose
+    workspace would exceed its 16 MiB array, before any HIP call."""
+    L = fm.lib()
+    d = fm.desc(2048, 768)
+    w = _weights()
+    call = lambda T, dd=d, ww=w, x=A, wr=A, y=A: L.flint_moe_layer_noalloc(
+        None if dd is None else ctypes.byref(dd), ctypes.byref(ww), T, x, wr, None, y, None, None)
+    assert call(0) == fm.OK
+    assert call(1, dd=None) == fm.ERR_NULL
+    assert call(-1) == fm.ERR_SHAPE
+    assert call(4, wr=None) == fm.ERR_NULL
+    assert call(4, y=MIS) == fm.ERR_ALIGN
+    assert fm.workspace_bytes(d, 180) <= 16 << 20 < fm.workspace_bytes(d, 256)
+    assert call(256) == fm.ERR_WORKSPACE
+    assert call(65536) == fm.ERR_WORKSPACE
