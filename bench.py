@@ -1,26 +1,36 @@
 #!/usr/bin/env python3
 """MoE-layer benchmark on one MI355X.
 
-Default workload: decode, T = 1 token per step through a stack of 47 distinct Flint-style
-MoE layers (H=2048, I=768, 256 routed experts, top-6 sigmoid routing + 1 shared expert,
-SwiGLU, bf16 weights N(0, 0.02), x ~ N(0, 1)).  The 47 layers hold 114 GB of expert
-weights, so every layer streams its experts from HBM.  One step = the whole hot path
-(router, top-k, grouping, experts, combine) for every layer of the stack, replayed from a
-HIP graph.  Inputs are seeded synthetic data drawn on the device before timing.
+The layer: Flint-style MoE FFN (H=2048, I=768, 256 routed experts, top-6 sigmoid routing + 1
+shared expert, SwiGLU), seeded synthetic weights N(0, 0.02) and tokens N(0, 1), drawn on the
+device before timing.  A step is the whole hot path (router, top-k, grouping, experts,
+combine) of every layer of a stack; decode workloads cycle 47 distinct layers (114 GB bf16,
+32 GB NVFP4), so every layer streams its experts from HBM, and prefill runs one layer of
+8192 tokens.  Steps are replayed from a HIP graph.
 
-Prints one JSON line: MoE-layer tokens/s, the roofline of the dominant kernel (bytes or
-flops per launch over its measured duration) and the reference's single-core CPU rate on
-a bounded sample.  --config picks another workload: decode_t8, decode_t32, prefill,
-prefill_zipf, nvfp4_t1, nvfp4_t8, nvfp4_t32, nvfp4_prefill, int4_t1, int4_t8, int4_t32, int4_prefill, and the dense SwiGLU layer
-(no router, I = 4096) at dense_t1, dense_t32, dense_prefill (and nvfp4_dense_t1, int4_dense_t1
-with 4-bit weights); chain_t1 and nvfp4_chain_t1
-run the single token through all 47 layers with one flint_moe_decode_chain call (token of
-layer l + 1 = bf16(x_l + y_l), formed in the kernel of layer l).
+The default run measures the whole metric in one JSON line: decode T=1 (the headline `value`),
+T=8, T=32, prefill T=8192 with uniform and with Zipf(1.1)-biased routing, and NVFP4 decode
+T=1/8/32.  Each workload is timed as `trials` (default 5) replays of a graph of K steps after
+W warm-up steps; the line reports the median trial (tokens/s, ms per step) with the IQR, the
+roofline (algorithmic HBM bytes or MFMA flops per layer call over the median layer time),
+and the reference timed single-threaded on the host on a bounded sample of the same
+workload.  It also reports a measured device-to-device copy bandwidth, the seed, the Zipf
+constant and SHA-256 digests of the input tokens and of the last layer's output.
+
+Other workloads through --configs: int4_t1/8/32, nvfp4_prefill, int4_prefill, dense_t1/t32/
+prefill (the dense SwiGLU layer, no router, I = 4096), nvfp4_dense_t1, int4_dense_t1, and
+chain_t1 / nvfp4_chain_t1 (one flint_moe_decode_chain call per step through the 47 layers).
+
+The timed trials of each workload sit between two flint_moe_workspace_status calls, whose
+one-thread kernel (ws_status_kernel) marks them in a rocprofv3 kernel trace or counter
+collection; --summarize-trace turns such a CSV into the markdown tables kept under
+profiles/, counting only the dispatches between the markers.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import platform
@@ -32,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 H, I, E, TOPK, S = 2048, 768, 256, 6, 1
 DENSE_I = 4096  # intermediate size of the dense SwiGLU layers (not given by the pages)
+SEED = 0
 CONFIGS = {
     "decode_t1": dict(T=1, fmt=0, layers=47, zipf=False),
     "decode_t8": dict(T=8, fmt=0, layers=47, zipf=False),
@@ -60,6 +71,24 @@ CONFIGS = {
     "nvfp4_dense_t1": dict(T=1, fmt=1, layers=48, zipf=False, dense=True),
     "int4_dense_t1": dict(T=1, fmt=2, layers=48, zipf=False, dense=True),
 }
+# the metric's workloads: decode T = 1 / 8 / 32 and the 8192-token prefill (uniform and
+# Zipf-biased routing) in bf16, and NVFP4 decode T = 1 / 8 / 32; the first is the headline
+DEFAULT_CONFIGS = ["decode_t1", "decode_t8", "decode_t32", "prefill", "prefill_zipf",
+                   "nvfp4_t1", "nvfp4_t8", "nvfp4_t32"]
+FMT_NAME = ("bf16", "NVFP4", "INT4")
+DTYPE = ("bf16",
+         "nvfp4-w4a16 (e2m1 weights with e4m3 block scales x bf16 activations, fp32 accumulate)",
+         "int4-w4a16 (int4 weights, bf16 scale per 128 columns, x bf16 activations, fp32 accumulate)")
+
+METRIC = "MoE-layer tokens/s at T=1/8/32/8192; achieved HBM GB/s or MFMA % of peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "sparse_moe_transformer_wave_amd", "csrc")
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
 def shape_of(cfg):
@@ -75,21 +104,12 @@ def expert_bytes(fmt, H_, I_):
     if fmt == 1:
         return 3 * (I_ * H_ // 2 + I_ * H_ // 16) + 3 * 4
     return 3 * (I_ * H_ // 2 + I_ * H_ // 64)
-METRIC = "MoE-layer tokens/s at T=1/8/32/8192; achieved HBM GB/s or MFMA % of peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-CSRC = os.path.join(ROOT, "sparse_moe_transformer_wave_amd", "csrc")
-HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
 
 
-def log(msg):
-    print("[bench] " + msg, file=sys.stderr, flush=True)
-
-
+# ------------------------------------------------------------------ counter traffic
 def csrc_digest():
     """sha256 over the HIP sources: counter-derived traffic is reported only while the
     kernels it was measured on are unchanged."""
-    import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h")):
@@ -124,119 +144,100 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
-def build_layer(torch, fm, dg, l, fmt, zipf, shp):
+def copy_bandwidth(torch, nbytes=4 << 30, reps=5):
+    """Device-to-device copy of nbytes (read + write = 2 nbytes moved), median of reps."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        b.copy_(a)
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e))
+    ts.sort()
+    ms = ts[len(ts) // 2]
+    del a, b
+    return {"bytes_moved": 2 * nbytes, "median_ms": round(ms, 4),
+            "GB_per_s": round(2 * nbytes / (ms / 1e3) / 1e9, 1),
+            "what": "torch device-to-device copy of %d GiB (read + write)" % (nbytes >> 30)}
+
+
+# ------------------------------------------------------------------ pools
+def build_layer(torch, fm, dg, l, fmt, shp):
     """Layer l of the seeded pool, drawn on the device."""
-    H, I, E, _, S = shp
-    d = {"Wr": None, "bias": None}
-    if E:
-        d["Wr"] = torch.empty((E, H), dtype=torch.float32, device="cuda")
-        dg.device_normal_f32(d["Wr"], 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
-        d["bias"] = torch.from_numpy(dg.zipf_bias(E, dg.ZIPF_C, 0, l)).cuda() if zipf else None
-    kinds = (("gate", dg.KIND_GATE, I, H), ("up", dg.KIND_UP, I, H), ("down", dg.KIND_DOWN, H, I))
+    H_, I_, E_, _, S_ = shp
+    d = {"Wr": None}
+    if E_:
+        d["Wr"] = torch.empty((E_, H_), dtype=torch.float32, device="cuda")
+        dg.device_normal_f32(d["Wr"], SEED, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
+    kinds = (("gate", dg.KIND_GATE, I_, H_), ("up", dg.KIND_UP, I_, H_), ("down", dg.KIND_DOWN, H_, I_))
+    n = E_ + S_
     if fmt == 0:
         for name, kind, N, K in kinds:
-            t = torch.empty((E + S, N, K), dtype=torch.int16, device="cuda")
-            dg.device_normal_bf16(t, E + S, N * K, 0, dg.stream_id(l, kind, 0), dg.W_STD)
+            t = torch.empty((n, N, K), dtype=torch.int16, device="cuda")
+            dg.device_normal_bf16(t, n, N * K, SEED, dg.stream_id(l, kind, 0), dg.W_STD)
             d[name] = t
-        if E == 0:  # dense layer: the shared expert's pointers only
-            d["weights"] = fm.Weights(0, None, None, None, d["gate"][0], d["up"][0], d["down"][0])
-        else:
-            d["weights"] = fm.Weights(0, d["gate"], d["up"], d["down"], d["gate"][E], d["up"][E],
-                                      d["down"][E])
+        r = [d["gate"], d["up"], d["down"]] if E_ else [None, None, None]
+        d["weights"] = fm.Weights(0, *r, d["gate"][E_], d["up"][E_], d["down"][E_])
     elif fmt == 2:
         for name, kind, N, K in kinds:
-            q = torch.empty((E + S, N, K // 2), dtype=torch.uint8, device="cuda")
-            sc = torch.empty((E + S, N, K // 128), dtype=torch.int16, device="cuda")
-            dg.device_int4(q, sc, E + S, N, K, 0, dg.stream_id(l, kind, 0), dg.W_STD)
+            q = torch.empty((n, N, K // 2), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((n, N, K // 128), dtype=torch.int16, device="cuda")
+            dg.device_int4(q, sc, n, N, K, SEED, dg.stream_id(l, kind, 0), dg.W_STD)
             d["q_" + name], d["sc_" + name] = q, sc
-        if E == 0:  # dense layer: the shared expert's pointers only
-            d["weights"] = fm.Weights(2, None, None, None, d["q_gate"][0], d["q_up"][0], d["q_down"][0],
-                                      None, None, None, d["sc_gate"][0], d["sc_up"][0], d["sc_down"][0])
-        else:
-            d["weights"] = fm.Weights(
-                2, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
-                d["sc_gate"], d["sc_up"], d["sc_down"], d["sc_gate"][E], d["sc_up"][E], d["sc_down"][E])
+        q = [d["q_gate"], d["q_up"], d["q_down"]] if E_ else [None] * 3
+        sc = [d["sc_gate"], d["sc_up"], d["sc_down"]] if E_ else [None] * 3
+        d["weights"] = fm.Weights(2, *q, d["q_gate"][E_], d["q_up"][E_], d["q_down"][E_],
+                                  *sc, d["sc_gate"][E_], d["sc_up"][E_], d["sc_down"][E_])
     else:
-        scratch = torch.empty(E + S, dtype=torch.int32, device="cuda")
+        scratch = torch.empty(n, dtype=torch.int32, device="cuda")
         for name, kind, N, K in kinds:
-            q = torch.empty((E + S, N, K // 2), dtype=torch.uint8, device="cuda")
-            sf = torch.empty((E + S, N, K // 16), dtype=torch.uint8, device="cuda")
-            ts = torch.empty(E + S + 3, dtype=torch.float32, device="cuda")
-            dg.device_nvfp4(q, sf, ts, scratch, E + S, N, K, 0, dg.stream_id(l, kind, 0), dg.W_STD)
+            q = torch.empty((n, N, K // 2), dtype=torch.uint8, device="cuda")
+            sf = torch.empty((n, N, K // 16), dtype=torch.uint8, device="cuda")
+            ts = torch.empty(n + 3, dtype=torch.float32, device="cuda")
+            dg.device_nvfp4(q, sf, ts, scratch, n, N, K, SEED, dg.stream_id(l, kind, 0), dg.W_STD)
             d["q_" + name], d["sf_" + name], d["ts_" + name] = q, sf, ts
-        sh_ts = torch.stack([d["ts_gate"][E], d["ts_up"][E], d["ts_down"][E]]).contiguous()
-        sh_ts = torch.cat([sh_ts, torch.zeros(1, device="cuda")])
-        d["sh_ts"] = sh_ts
-        if E == 0:  # dense layer: the shared expert's pointers only
-            d["weights"] = fm.Weights(
-                1, None, None, None, d["q_gate"][0], d["q_up"][0], d["q_down"][0], None, None, None,
-                d["sf_gate"][0], d["sf_up"][0], d["sf_down"][0], None, None, None, sh_ts)
-        else:
-            d["weights"] = fm.Weights(
-                1, d["q_gate"], d["q_up"], d["q_down"], d["q_gate"][E], d["q_up"][E], d["q_down"][E],
-                d["sf_gate"], d["sf_up"], d["sf_down"], d["sf_gate"][E], d["sf_up"][E],
-                d["sf_down"][E], d["ts_gate"], d["ts_up"], d["ts_down"], sh_ts)
+        sh_ts = torch.stack([d["ts_gate"][E_], d["ts_up"][E_], d["ts_down"][E_]]).contiguous()
+        d["sh_ts"] = torch.cat([sh_ts, torch.zeros(1, device="cuda")])
+        q = [d["q_gate"], d["q_up"], d["q_down"]] if E_ else [None] * 3
+        sf = [d["sf_gate"], d["sf_up"], d["sf_down"]] if E_ else [None] * 3
+        ts = [d["ts_gate"], d["ts_up"], d["ts_down"]] if E_ else [None] * 3
+        d["weights"] = fm.Weights(1, *q, d["q_gate"][E_], d["q_up"][E_], d["q_down"][E_], *sf,
+                                  d["sf_gate"][E_], d["sf_up"][E_], d["sf_down"][E_], *ts, d["sh_ts"])
     return d
 
 
-def cpu_baseline(cfg, budget_s):
-    """The reference (single-threaded C, fp64) on a bounded sample of the same workload:
-    the whole layer (router, selection, weights, experts, combine) for cfg's T tokens
-    through layers 0..7 of the stack, cycled until budget_s of reference time."""
-    import numpy as np
+class Pools:
+    """Device pools, built once per (format, dense) and shared by the workloads that use
+    them (the prefill runs on layer 0 of the decode stack)."""
 
-    import oracle
-    from sparse_moe_transformer_wave_amd import datagen as dg
-    H, I, E, TOPK, S = shape_of(cfg)
-    nvfp4 = cfg["fmt"] == 1
-    int4 = cfg["fmt"] == 2
-    # host quantisation costs ~1 s per expert: NVFP4 samples 2 tokens of one layer
-    T = min(cfg["T"], 2) if nvfp4 else cfg["T"] if cfg["T"] <= 32 else 4
-    n_layers = min(1 if nvfp4 else 8, cfg["layers"])
-    x = dg.normal_bf16((cfg["T"], H), 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)[:T]
-    x = np.ascontiguousarray(x)
-    if E == 0:
-        return cpu_baseline_dense(cfg, budget_s, x, H, I, n_layers)
-    layers = []
-    for l in range(n_layers):
-        Wr = dg.normal_f32((E, H), 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
-        bias = dg.zipf_bias(E, dg.ZIPF_C, 0, l) if cfg["zipf"] else None
-        ids = oracle.select(oracle.router(x, Wr, bias), TOPK)
-        used = sorted(set(ids.reshape(-1).tolist()))
-        local = {e: i for i, e in enumerate(used)}
-        arrays = {}
-        for e in used + [E]:
-            for name, kind, shape in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
-                                      ("down", dg.KIND_DOWN, (H, I))):
-                if nvfp4:
-                    q, sb, st = oracle.nvfp4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
-                    for pre, v in (("q_", q), ("sb_", sb), ("st_", np.float32(st))):
-                        arrays.setdefault(pre + name, []).append(v)
-                elif int4:
-                    q, sb = oracle.int4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
-                    for pre, v in (("q_", q), ("sb_", sb)):
-                        arrays.setdefault(pre + name, []).append(v)
-                else:
-                    arrays.setdefault(name, []).append(dg.normal_bf16(shape, 0, dg.stream_id(l, kind, e), dg.W_STD))
-        fmt_o = oracle.FMT_NVFP4 if nvfp4 else oracle.FMT_INT4 if int4 else oracle.FMT_BF16
-        routed = oracle.Experts(fmt_o, H, I, {k: np.stack(v[:-1]) for k, v in arrays.items()})
-        shared = oracle.Experts(fmt_o, H, I, {k: np.stack(v[-1:]) for k, v in arrays.items()})
-        layers.append((Wr, bias, local, routed, shared))
-    done, t_used = 0, 0.0
-    while t_used < budget_s:
-        Wr, bias, local, routed, shared = layers[done % n_layers]
-        t0 = time.perf_counter()
-        logits = oracle.router(x, Wr, bias)
-        ids = oracle.select(logits, TOPK)
-        w = oracle.weights(logits, ids, True)
-        lid = np.vectorize(local.get)(ids).astype(np.int32)
-        oracle.moe_tokens(routed, shared, x, lid, w)
-        t_used += time.perf_counter() - t0
-        done += 1
-    return cpu_result(T, done, n_layers, t_used, "full layer, NVFP4 weights" if nvfp4 else
-                      "full layer, INT4 weights" if int4 else "full layer")
+    def __init__(self, torch, fm, dg):
+        self.torch, self.fm, self.dg = torch, fm, dg
+        self.pools = {}
+
+    def layers(self, cfg):
+        key = (cfg["fmt"], bool(cfg.get("dense")))
+        want = cfg["layers"]
+        have = self.pools.get(key, [])
+        if len(have) < want:
+            t0 = time.time()
+            shp = shape_of(cfg)
+            have = have + [build_layer(self.torch, self.fm, self.dg, l, cfg["fmt"], shp)
+                           for l in range(len(have), want)]
+            self.torch.cuda.synchronize()
+            self.pools[key] = have
+            log("pool %s%s: %d layers, %.1f GB of expert weights, drawn in %.1f s"
+                % (FMT_NAME[cfg["fmt"]], " dense" if key[1] else "", want,
+                   want * (shp[2] + shp[4]) * expert_bytes(cfg["fmt"], shp[0], shp[1]) / 1e9, time.time() - t0))
+        return have[:want]
 
 
+# ------------------------------------------------------------------ reference on the host
 def host_cpu():
     cpu = platform.processor() or platform.machine()
     try:
@@ -249,48 +250,319 @@ def host_cpu():
     return cpu
 
 
-def cpu_result(T, done, n_layers, t_used, what):
-    return {"value": T * done / t_used, "unit": "MoE-layer tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d token(s) x %d layer evaluations (layers 0..%d cycled), %s, "
-                      "single-threaded fp64 C reference, %.1f s; host CPU %s, %d logical cores"
-                      % (T, done, n_layers - 1, what, t_used, host_cpu(), os.cpu_count() or 0)}
+def experts_to_host(torch, oracle, d, idx, fmt, H_, I_):
+    """The listed experts of a device layer, copied back as the reference's expert arrays."""
+    ix = torch.tensor(idx, dtype=torch.long, device="cuda")
+    a = {}
+    for name in ("gate", "up", "down"):
+        if fmt == 0:
+            a[name] = d[name][ix].cpu().numpy().view("uint16")
+        elif fmt == 1:
+            a["q_" + name] = d["q_" + name][ix].cpu().numpy()
+            a["sb_" + name] = d["sf_" + name][ix].cpu().numpy()
+            a["st_" + name] = d["ts_" + name][ix].cpu().numpy()
+        else:
+            a["q_" + name] = d["q_" + name][ix].cpu().numpy()
+            a["sb_" + name] = d["sc_" + name][ix].cpu().numpy().view("uint16")
+    return oracle.Experts((oracle.FMT_BF16, oracle.FMT_NVFP4, oracle.FMT_INT4)[fmt], H_, I_, a)
 
 
-def cpu_baseline_dense(cfg, budget_s, x, H, I, n_layers):
-    """The reference's SwiGLU expert (the dense layer) for each token, layers cycled; 4-bit
-    weights are quantised on the host by the reference's own quantisers."""
+def cpu_baseline(torch, cfg, layers, x_host, budget_s):
+    """The reference (single-threaded C, fp64) on a bounded sample of the same workload and
+    the same bytes (the touched experts copied back from the device pool): the whole layer
+    (router, selection, weights, experts, combine) for up to 32 of the tokens, layers cycled
+    until budget_s of reference time."""
     import numpy as np
 
     import oracle
-    from sparse_moe_transformer_wave_amd import datagen as dg
-    fmt = cfg["fmt"]
-    layers = []
+    H_, I_, E_, k_, S_ = shape_of(cfg)
+    T = cfg["T"] if cfg["T"] <= 32 else 4
+    x = np.ascontiguousarray(x_host[:T])
+    n_layers = min(len(layers), 8 if T == 1 else 2 if T <= 8 else 1)
+    prep = []
     for l in range(n_layers):
-        arrays = {}
-        for name, kind, shape in (("gate", dg.KIND_GATE, (I, H)), ("up", dg.KIND_UP, (I, H)),
-                                  ("down", dg.KIND_DOWN, (H, I))):
-            if fmt == 0:
-                arrays[name] = dg.normal_bf16(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD)[None]
-            elif fmt == 1:
-                q, sb, st = oracle.nvfp4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD))
-                arrays["q_" + name], arrays["sb_" + name] = q[None], sb[None]
-                arrays["st_" + name] = np.array([st], dtype=np.float32)
-            else:
-                q, sb = oracle.int4_quantize(dg.normal_f64(shape, 0, dg.stream_id(l, kind, 0), dg.W_STD))
-                arrays["q_" + name], arrays["sb_" + name] = q[None], sb[None]
-        fmt_o = (oracle.FMT_BF16, oracle.FMT_NVFP4, oracle.FMT_INT4)[fmt]
-        layers.append(oracle.Experts(fmt_o, H, I, arrays))
-    xf = dg.bf16_bits_to_f32(x).astype(np.float64)
+        d = layers[l]
+        if E_ == 0:
+            prep.append((None, None, None, experts_to_host(torch, oracle, d, [0], cfg["fmt"], H_, I_)))
+            continue
+        Wr = d["Wr"].cpu().numpy()
+        bias = d.get("bias")
+        bias = None if bias is None else bias.cpu().numpy()
+        ids = oracle.select(oracle.router(x, Wr, bias), k_)
+        used = sorted(set(ids.reshape(-1).tolist()))
+        local = np.zeros(E_, np.int32)
+        local[used] = np.arange(len(used), dtype=np.int32)
+        routed = experts_to_host(torch, oracle, d, used, cfg["fmt"], H_, I_)
+        shared = experts_to_host(torch, oracle, d, [E_], cfg["fmt"], H_, I_)
+        prep.append((Wr, bias, local, (routed, shared)))
+    xf = x.view(np.uint16)
     done, t_used = 0, 0.0
-    while t_used < budget_s:
-        ex = layers[done % n_layers]
+    while t_used < budget_s or done == 0:
+        Wr, bias, local, ex = prep[done % n_layers]
         t0 = time.perf_counter()
-        for t in range(x.shape[0]):
-            oracle.expert_ffn(ex, 0, xf[t])
+        if E_ == 0:
+            xd = (xf.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            for t in range(T):
+                oracle.expert_ffn(ex, 0, xd[t])
+        else:
+            logits = oracle.router(x, Wr, bias)
+            ids = oracle.select(logits, k_)
+            w = oracle.weights(logits, ids, True)
+            oracle.moe_tokens(ex[0], ex[1], x, local[ids], w)
         t_used += time.perf_counter() - t0
         done += 1
-    return cpu_result(x.shape[0], done, n_layers, t_used, ("dense SwiGLU layer", "dense SwiGLU layer, NVFP4 weights",
-                                                          "dense SwiGLU layer, INT4 weights")[fmt])
+    what = ("dense SwiGLU layer" if E_ == 0 else "full layer") + (", %s weights" % FMT_NAME[cfg["fmt"]])
+    tok_note = "" if cfg["T"] <= 32 else " (the first %d of the batch's %d tokens)" % (T, cfg["T"])
+    return {"value": T * done / t_used, "unit": "MoE-layer tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d token(s)%s x %d layer evaluations (layers 0..%d cycled), %s, single-threaded "
+                      "fp64 C reference on the device pool's bytes, %.1f s; host CPU %s, %d logical cores"
+                      % (T, tok_note, done, n_layers - 1, what, t_used, host_cpu(), os.cpu_count() or 0)}
+
+
+# ------------------------------------------------------------------ one workload
+def sha256_of(t):
+    return hashlib.sha256(t.contiguous().cpu().numpy().tobytes()).hexdigest()
+
+
+def run_config(name, args, torch, fm, dg, pools):
+    import numpy as np
+    cfg = CONFIGS[name]
+    T, fmt, L = cfg["T"], cfg["fmt"], cfg["layers"]
+    shp = shape_of(cfg)
+    H_, I_, E_, k_, S_ = shp
+    chain = bool(cfg.get("chain"))
+    log("config %s: T=%d %s, %d layer(s)%s" % (name, T, FMT_NAME[fmt], L, ", chained" if chain else ""))
+    layers = pools.layers(cfg)
+    bias = None
+    if cfg["zipf"]:
+        bias = torch.from_numpy(dg.zipf_bias(E_, dg.ZIPF_C, SEED, 0)).cuda()
+    for d in layers:
+        d["bias"] = bias
+    x = torch.empty((T, H_), dtype=torch.int16, device="cuda")
+    dg.device_normal_bf16(x, 1, T * H_, SEED, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
+    y = torch.empty((T, H_), dtype=torch.int16, device="cuda")
+    desc = fm.desc(H_, I_, E_, k_, S_, 1)
+    ws = fm.workspace(desc, T, fmt)
+
+    # Routing of every layer (for the algorithmic bytes: distinct experts touched), outside
+    # the timed region.
+    touched = []
+    if E_ and not chain:
+        counts = torch.zeros(E_, dtype=torch.int32, device="cuda")
+        for d in layers:
+            fm.layer(desc, d["weights"], T, x, d["Wr"], d["bias"], y, ws, {"counts": counts})
+            touched.append(int((counts > 0).sum().item()))
+    else:
+        touched = [TOPK if E_ else 0] * L  # a single token touches exactly k routed experts
+    xb = expert_bytes(fmt, H_, I_)
+    alg_bytes = [(u + S_) * xb + E_ * H_ * 4 + 4 * T * H_ for u in touched]
+    flops_layer = 2.0 * T * (k_ + S_) * 3 * H_ * I_
+    ychain = None
+    L_lib = fm.lib()
+    if chain:
+        ychain = torch.empty((L, H_), dtype=torch.int16, device="cuda")
+        refs = fm.layer_refs([(d["weights"], d["Wr"], d["bias"]) for d in layers])
+
+    def capture(n_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = torch.cuda.current_stream().cuda_stream
+            if chain:
+                fn, fname = L_lib.flint_moe_decode_chain, "flint_moe_decode_chain"
+                calls = [((ctypes.byref(desc), refs, L, fm.CHAIN_RESIDUAL, x.data_ptr(), ychain.data_ptr(),
+                           None, None, None, ws.data_ptr(), ws.numel(), st), refs)]
+            else:
+                fn, fname = L_lib.flint_moe_layer, "flint_moe_layer"
+                calls = [fm.layer_ptr_args(desc, d["weights"], T, x, d["Wr"], d["bias"], y,
+                                           ws.data_ptr(), ws.numel(), st) for d in layers]
+            for _ in range(n_steps):
+                for a, _keep in calls:
+                    rc = fn(*a)
+                    if rc:
+                        raise fm.FlintError(rc, fname)
+        return g, calls
+
+    g_warm, keep_w = capture(1)
+    g_timed, keep_t = capture(args.steps)
+    for _ in range(args.warmup):
+        g_warm.replay()
+    torch.cuda.synchronize()
+    # the status call's kernel marks the start of the timed trials in a kernel trace (and
+    # checks that no persistent launch timed out during the warm-up)
+    assert fm.workspace_status(ws) == 0, "a persistent launch's wait ran out during the warm-up"
+    times = []
+    for _ in range(args.trials):
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g_timed.replay()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    status = fm.workspace_status(ws)  # the end marker
+    assert status == 0, "a persistent launch's wait ran out during the timed trials"
+    q25, med, q75 = (float(v) for v in np.percentile(times, [25, 50, 75]))
+    K = args.steps
+    layer_ms = med / (K * L)
+    out = {
+        "value": round(T * L * K / (med / 1e3), 1), "unit": "MoE-layer tokens/s",
+        "ms_per_step": round(med / K, 4), "dtype": DTYPE[fmt] if fmt else "bf16",
+        "trials": {"n": args.trials, "median_ms": round(med, 4), "iqr_ms": round(q75 - q25, 4),
+                   "all_ms": [round(t, 4) for t in times], "layer_us_median": round(layer_ms * 1e3, 2)},
+        "config": {
+            "workload": ("%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, SwiGLU, %s, "
+                         "%d distinct layer(s)%s" % (name, T, H_, I_, E_, k_, S_, FMT_NAME[fmt], L,
+                                                     ", Zipf(1.1) logit bias (c = %.4f)" % dg.ZIPF_C if cfg["zipf"] else
+                                                     ", chained: one flint_moe_decode_chain call per step, token "
+                                                     "of layer l + 1 = bf16(x_l + y_l)" if chain else ""))
+            if E_ else ("%s: T=%d tokens, dense SwiGLU FFN layer (no router), H=%d, I=%d, %s, %d distinct layers"
+                        % (name, T, H_, I_, FMT_NAME[fmt], L)),
+            "tokens_per_layer_call": T, "layers": L, "touched_experts_mean": float(np.mean(touched))},
+    }
+    if T <= 32:
+        bytes_per_call = sum(alg_bytes) / L
+        achieved = bytes_per_call / (layer_ms / 1e3) / 1e9
+        kernel = ("dense1_kernel (the whole dense layer in one persistent launch)" if E_ == 0 and T == 1 else
+                  "the dense layer's gate/up and down kernels" if E_ == 0 else
+                  "decode1_kernel (one persistent launch per layer; chain time / layers)" if chain else
+                  "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
+                  "one layer call: router with selection, gate/up, down and combine kernels")
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
+                           "kernel": kernel, "avg_launch_us": round(layer_ms * 1e3, 2),
+                           "alg_bytes_per_launch": int(bytes_per_call)}
+    else:
+        achieved = flops_layer / (layer_ms / 1e3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                           "traffic": measured_traffic(name),
+                           "kernel": "one layer call: router, top-k, grouping, gate/up and down GEMMs, combine",
+                           "avg_launch_us": round(layer_ms * 1e3, 2), "alg_flops_per_launch": flops_layer,
+                           "alg_bytes_per_launch": int(sum(alg_bytes) / L),
+                           "hbm_floor_us": round(sum(alg_bytes) / L / (HBM_PEAK_GBS * 1e9) * 1e6, 1)}
+    out["sha256"] = {"x": sha256_of(x), "y_last_layer": sha256_of(ychain[-1:] if chain else y)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(torch, cfg, layers, x.cpu().numpy().view("uint16"), args.cpu_seconds)
+    log("  %s: %.1f tokens/s, %.2f us per layer (IQR %.4f ms over %d trials), %s %.3f of peak"
+        % (name, out["value"], layer_ms * 1e3, q75 - q25, args.trials, out["roofline"]["unit"],
+           out["roofline"]["frac"]))
+    del keep_w, keep_t, g_warm, g_timed
+    return out
+
+
+# ------------------------------------------------------------------ profile summaries
+MARKER = "ws_status_kernel"
+
+
+def short_kernel_name(n):
+    """A rocprofv3 kernel name without return type, namespaces and parameter list."""
+    if n.startswith("void "):
+        n = n[5:]
+    n = n.replace("(anonymous namespace)::", "").replace("flint::", "")
+    n = n.split("(")[0]
+    return n if len(n) <= 60 else n[:57] + "..."
+
+
+def summarize_trace(csv_path, title, command, note=""):
+    """Markdown table of the kernels of a rocprofv3 kernel trace (kernel_trace.csv) or counter
+    collection (counter_collection.csv) that ran between the first two ws_status_kernel
+    dispatches, i.e. inside the timed trials of one workload.  For a counter collection the
+    table gives each kernel's mean counter value per dispatch."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    name_key = "Kernel_Name"
+    start_key = "Start_Timestamp"
+    end_key = "End_Timestamp"
+    rows.sort(key=lambda r: int(r[start_key]))
+    marks = [i for i, r in enumerate(rows) if MARKER in r[name_key]]
+    if len(marks) < 2:
+        raise SystemExit("%s: fewer than two %s dispatches" % (csv_path, MARKER))
+    inside = rows[marks[0] + 1:marks[1]]
+    counters = "Counter_Name" in rows[0]
+    per = {}
+    for r in inside:
+        nm = r[name_key]
+        if counters:
+            nm = (nm, r["Counter_Name"])
+        per.setdefault(nm, []).append(float(r["Counter_Value"]) if counters else
+                                      (int(r[end_key]) - int(r[start_key])) / 1e3)
+    window_us = (int(rows[marks[1]][start_key]) - int(rows[marks[0]][end_key])) / 1e3
+    note_extra = ("The at::native fill and __amd_rocclr_copyBuffer dispatches in the window are the status "
+                  "call's own (its output word is zeroed before and copied to the host after it).")
+    note = (note + "\n\n" + note_extra) if note else note_extra
+    lines = ["# %s" % title, "", "Command (from the repository root, on one MI355X):", "", "```", command, "```", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["Dispatches between the two %s markers (the timed trials only): %d, over %.1f us."
+              % (MARKER, len(inside), window_us), ""]
+
+    if counters:
+        lines += ["| kernel | counter | dispatches | mean per dispatch (KiB) | total (KiB) |", "|---|---|---|---|---|"]
+        for (nm, ctr), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("| %s | %s | %d | %.1f | %.1f |" % (short_kernel_name(nm), ctr, len(v), sum(v) / len(v), sum(v)))
+    else:
+        tot = sum(sum(v) for v in per.values())
+        lines += ["| kernel | calls | avg us | min us | max us | % of kernel time |", "|---|---|---|---|---|---|"]
+        for nm, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (short_kernel_name(nm), len(v), sum(v) / len(v), min(v),
+                                                                   max(v), 100.0 * sum(v) / tot))
+    return "\n".join(lines) + "\n"
+
+
+def _marked_rows(csv_path):
+    """Rows of a rocprofv3 CSV between the first two marker dispatches, by start time."""
+    import csv
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    marks = [i for i, r in enumerate(rows) if MARKER in r["Kernel_Name"]]
+    if len(marks) < 2:
+        raise SystemExit("%s: fewer than two %s dispatches" % (csv_path, MARKER))
+    return rows[marks[0] + 1:marks[1]]
+
+
+def traffic_json(copy_fetch_csv, copy_write_csv, entries):
+    """HBM traffic per layer call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs (KiB per
+    dispatch), each counter scaled so that a plain 1 GiB device copy (bench.py
+    --copy-calibration) reads and writes 1 GiB.  entries: NAME=FETCH_CSV,WRITE_CSV strings.
+    The layer calls inside the marked window are counted as the fewest dispatches of any one
+    of the library's kernels there (every kernel of a layer call runs once per call); the
+    status call's own torch and runtime dispatches are left out."""
+    import csv
+    calib = {}
+    for ctr, path in (("FETCH_SIZE", copy_fetch_csv), ("WRITE_SIZE", copy_write_csv)):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if "copy" in r["Kernel_Name"].lower() and r["Counter_Name"] == ctr]
+        top = max(vals)
+        calib[ctr] = {"copy_1GiB_counter_KiB": top, "scale": (1 << 20) / top}
+    out = {"csrc_sha256": csrc_digest(),
+           "made_by": [
+               "rocprofv3 --pmc COUNTER --output-format csv -d gpurun_out/prof/pmc_copy_COUNTER -o run -- "
+               "python3 bench.py --copy-calibration",
+               "rocprofv3 --pmc COUNTER --output-format csv -d gpurun_out/prof/pmc_NAME_COUNTER -o run -- "
+               "python3 bench.py --configs NAME --no-cpu-baseline --no-copy-bandwidth --steps 2 --warmup 1 --trials 1",
+               "(COUNTER = FETCH_SIZE, then WRITE_SIZE, one run each), then python3 bench.py --traffic " +
+               " ".join([copy_fetch_csv, copy_write_csv] + list(entries))],
+           "calibration": calib, "configs": {}}
+    for ent in entries:
+        name, paths = ent.split("=", 1)
+        per_kernel, calls, total = {}, None, 0.0
+        for ctr, path in zip(("FETCH_SIZE", "WRITE_SIZE"), paths.split(",")):
+            counts = {}
+            for r in _marked_rows(path):
+                if r["Counter_Name"] != ctr or "flint::" not in r["Kernel_Name"]:
+                    continue
+                b = float(r["Counter_Value"]) * calib[ctr]["scale"] * 1024.0
+                k = short_kernel_name(r["Kernel_Name"])
+                per_kernel.setdefault(k, {}).setdefault(ctr, 0.0)
+                per_kernel[k][ctr] += b
+                counts[k] = counts.get(k, 0) + 1
+                total += b
+            n = min(counts.values())
+            calls = n if calls is None else min(calls, n)
+        out["configs"][name] = {
+            "layer_calls_counted": calls, "bytes_per_layer_call": int(round(total / calls)),
+            "per_kernel_bytes_per_layer_call": {k: {c: int(round(v / calls)) for c, v in d.items()}
+                                                for k, d in per_kernel.items()}}
+    return out
 
 
 def main():
@@ -298,12 +570,28 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="decode_t1", choices=sorted(CONFIGS))
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--trials", type=int, default=5)
+    ap.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
+                    help="comma-separated workloads; the first is the headline (default: the metric's set)")
+    ap.add_argument("--config", default=None, help="a single workload (same as --configs NAME)")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="reference time budget per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-bandwidth", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--traffic", nargs="+", metavar="ARG",
+                    help="COPY_FETCH_CSV COPY_WRITE_CSV NAME=FETCH_CSV,WRITE_CSV ...: print the counter "
+                         "traffic JSON (profiles/traffic.json) and exit")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                    help="CSV TITLE COMMAND [NOTE]: print the markdown summary of the timed trials in a "
+                         "rocprofv3 kernel_trace.csv or counter_collection.csv and exit")
     args = ap.parse_args()
+    if args.traffic:
+        print(json.dumps(traffic_json(args.traffic[0], args.traffic[1], args.traffic[2:]), indent=1))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace), end="")
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -311,155 +599,41 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    names = [args.config] if args.config else [c for c in args.configs.split(",") if c]
+    for n in names:
+        if n not in CONFIGS:
+            sys.exit("unknown workload %s (known: %s)" % (n, ", ".join(sorted(CONFIGS))))
 
-    import numpy as np
     import torch
 
     import sparse_moe_transformer_wave_amd as fm
     from sparse_moe_transformer_wave_amd import datagen as dg
 
-    cfg = CONFIGS[args.config]
-    T, fmt, L = cfg["T"], cfg["fmt"], cfg["layers"]
-    shp = shape_of(cfg)
-    H, I, E, TOPK, S = shp
     torch.cuda.init()
-    log("config %s: T=%d fmt=%s layers=%d" % (args.config, T, ("bf16", "nvfp4", "int4")[fmt], L))
-    t0 = time.time()
-    layers = [build_layer(torch, fm, dg, l, fmt, cfg["zipf"], shp) for l in range(L)]
-    x = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    dg.device_normal_bf16(x, 1, T * H, 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
-    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    desc = fm.desc(H, I, E, TOPK, S, 1)
-    ws = fm.workspace(desc, T, fmt)
-    torch.cuda.synchronize()
-    xb = expert_bytes(fmt, H, I)
-    log("pool ready (%.1f GB of expert weights) in %.1f s"
-        % (L * (E + S) * xb / 1e9, time.time() - t0))
-
-    # Routing of every layer (for the algorithmic byte count: distinct experts touched).
-    touched = []
-    if E:
-        counts = torch.zeros(E, dtype=torch.int32, device="cuda")
-        for d in layers:
-            fm.layer(desc, d["weights"], T, x, d["Wr"], d["bias"], y, ws, {"counts": counts})
-            touched.append(int((counts > 0).sum().item()))
-    else:
-        for d in layers:
-            fm.layer(desc, d["weights"], T, x, None, None, y, ws)
-            touched.append(0)
-    chain = bool(cfg.get("chain"))
-    if chain:  # a single token touches exactly k routed experts in every layer
-        touched = [TOPK] * L
-        ychain = torch.empty((L, H), dtype=torch.int16, device="cuda")
-        refs = fm.layer_refs([(d["weights"], d["Wr"], d["bias"]) for d in layers])
-    alg_bytes = [(u + S) * xb + E * H * 4 + 4 * T * H for u in touched]
-    flops_layer = 2.0 * T * (TOPK + S) * 3 * H * I
-
-    stream = torch.cuda.current_stream()
-    L_lib = fm.lib()
-
-    def capture(n_steps, with_events):
-        ev = []
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            st = torch.cuda.current_stream().cuda_stream
-            if chain:
-                fn, name = L_lib.flint_moe_decode_chain, "flint_moe_decode_chain"
-                calls = [((ctypes.byref(desc), refs, L, fm.CHAIN_RESIDUAL, x.data_ptr(), ychain.data_ptr(),
-                           None, None, None, ws.data_ptr(), ws.numel(), st), refs)]
-            else:
-                fn, name = L_lib.flint_moe_layer, "flint_moe_layer"
-                calls = [fm.layer_ptr_args(desc, d["weights"], T, x, d["Wr"], d["bias"], y,
-                                           ws.data_ptr(), ws.numel(), st) for d in layers]
-            for _ in range(n_steps):
-                for a, _keep in calls:
-                    if with_events:
-                        e = torch.cuda.Event(enable_timing=True, external=True)
-                        e.record()
-                        ev.append(e)
-                    rc = fn(*a)
-                    if rc:
-                        raise fm.FlintError(rc, name)
-            if with_events:
-                e = torch.cuda.Event(enable_timing=True, external=True)
-                e.record()
-                ev.append(e)
-        return g, ev, calls
-
-    g_warm, _, keep_w = capture(1, False)
-    try:
-        g_timed, evs, keep_t = capture(args.steps, True)
-    except RuntimeError as exc:  # no event nodes in graphs: time whole replays only
-        log("events inside the graph unavailable (%s); per-call time = replay / calls" % exc)
-        torch.cuda.synchronize()
-        g_timed, evs, keep_t = capture(args.steps, False)
-    log("graphs captured (%d + %d layer calls)" % (L, L * args.steps))
-    for _ in range(args.warmup):
-        g_warm.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    g_timed.replay()
-    end.record()
-    torch.cuda.synchronize()
-    elapsed_ms = start.elapsed_time(end)
-    if evs:
-        per_call = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)]
-        if chain:  # one event interval per chain call of L layers
-            per_call = [t / L for t in per_call for _ in range(L)]
-    else:
-        per_call = [elapsed_ms / (L * args.steps)] * (L * args.steps)
-    log("timed %d steps: %.3f ms" % (args.steps, elapsed_ms))
-
-    K = args.steps
-    tokens = T * L * K
-    value = tokens / (elapsed_ms / 1e3)
-    avg_call_ms = sum(per_call) / len(per_call)
-    if T <= 32:
-        bytes_per_call = sum(alg_bytes) / L
-        achieved = bytes_per_call / (avg_call_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
-                "kernel": ("dense1_kernel (the whole dense layer in one persistent launch)" if E == 0 and T == 1 else
-                           "flint_moe_layer (dense: gate/up and down kernels)" if E == 0 else
-                           "decode1_kernel (one persistent launch per layer; chain call time / layers)"
-                           if chain else
-                           "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
-                           "flint_moe_layer (router with selection, gate/up, down, combine kernels)"),
-                "avg_launch_us": round(avg_call_ms * 1e3, 2),
-                "alg_bytes_per_launch": int(bytes_per_call)}
-    else:
-        achieved = flops_layer / (avg_call_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.config),
-                "kernel": "flint_moe_layer (one layer: all kernels)",
-                "avg_launch_us": round(avg_call_ms * 1e3, 2), "alg_flops_per_launch": flops_layer}
+    pools = Pools(torch, fm, dg)
+    results = {}
+    for n in names:
+        results[n] = run_config(n, args, torch, fm, dg, pools)
+    head = results[names[0]]
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "MoE-layer tokens/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed_ms / K, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("bf16" if fmt == 0 else "nvfp4-w4a16 (e2m1 weights x bf16 activations, fp32 accumulate)"
-                  if fmt == 1 else "int4-w4a16 (int4 weights, bf16 scale per 128, x bf16 activations, fp32 accumulate)"),
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tokens, drawn on device)",
-        "config": {"workload": ("%s: T=%d tokens, H=%d, I=%d, E=%d routed, top-%d sigmoid + %d shared, "
-                                "SwiGLU, %s, %d distinct layers cycled%s"
-                                % (args.config, T, H, I, E, TOPK, S, ("bf16", "NVFP4", "INT4")[fmt],
-                                   L, ", Zipf(1.1) logit bias" if cfg["zipf"] else
-                                   ", chained: one flint_moe_decode_chain call per step, token of layer l + 1 = "
-                                   "bf16(x_l + y_l)" if chain else "")) if E else
-                               ("%s: T=%d tokens, dense SwiGLU FFN layer (no router), H=%d, I=%d, "
-                                "%s, %d distinct layers cycled" % (args.config, T, H, I,
-                                                                   "bf16" if fmt == 0 else "NVFP4", L)),
-                   "tokens_per_layer_call": T, "layers": L, "touched_experts_mean": float(np.mean(touched))},
-        "roofline": roof,
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) tokens, drawn on the device; seed %d)" % SEED,
+        "config": head["config"], "roofline": head["roofline"], "trials": head["trials"],
     }
-    if not args.no_cpu_baseline:
-        log("timing the reference on the host (%.0f s budget)" % args.cpu_seconds)
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    out["seed"] = SEED
+    out["zipf_c"] = dg.ZIPF_C
+    prop = torch.cuda.get_device_properties(0)
+    out["gpu"] = "%s%s, %d CUs, %.0f GB" % (torch.cuda.get_device_name() + " " if torch.cuda.get_device_name() else "",
+                                            getattr(prop, "gcnArchName", "?"), prop.multi_processor_count,
+                                            prop.total_memory / 1e9)
+    if not args.no_copy_bandwidth:
+        out["copy_bandwidth"] = copy_bandwidth(torch)
+    out["configs"] = results
     print(json.dumps(out), flush=True)
-    del keep_w, keep_t
 
 
 if __name__ == "__main__":

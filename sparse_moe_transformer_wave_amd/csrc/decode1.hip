@@ -27,12 +27,14 @@
 // written with agent-scope stores and polled with agent-scope loads: one aligned 64-bit
 // access carries the payload and its readiness together, so there are no grid barriers,
 // fences or cache-wide write-backs, and a reader waits one round trip after the word it
-// needs lands.  Each workgroup takes one ticket from the workspace head's ticket counter
-// when it starts; a launch has exactly 256 workgroups, so the 256 tickets of one launch
-// share ticket / 256, which gives the launch its tag.  A workgroup that starts late still
-// takes a ticket of its own launch (the next launch on the stream starts after every
-// workgroup of this one has ended), so a word it publishes never carries a later launch's
-// tag.  Every wait is bounded: on timeout the kernel sets the head's error flag (read and
+// needs lands.  The launch's tag comes from the workspace head's launch counters: workgroup
+// b reads counter b when it starts and writes it back plus one, and every persistent launch
+// has exactly 256 workgroups, so every counter holds the number of earlier launches and all
+// workgroups of a launch compute the same tag.  A workgroup that starts late still reads its
+// own launch's count (only workgroup b of the next launch could change counter b, and the
+// next launch on the stream starts after this one has ended), so a word it publishes never
+// carries a later launch's tag.  No two workgroups touch one counter, so nothing contends
+// for it.  Every wait is bounded: on timeout the kernel sets the head's error flag (read and
 // cleared by flint_moe_workspace_status) and carries on with the values it has.  All 256
 // workgroups must be resident together (one per CU): the host checks the CU count and the
 // kernel's occupancy before choosing this launch.
@@ -62,13 +64,19 @@ constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
 constexpr size_t kXLogOff = kHeadXchg, kXHOff = kXLogOff + 8 * kG;
 constexpr size_t kXNextOff = kXHOff + 8 * (size_t)(kMaxK + 1) * 1024;
 static_assert(kXNextOff + 2 * 2048 <= kSyncBytes, "exchange words exceed the head");
-static_assert(kG == kPersistentGrid, "one ticket per workgroup of a persistent launch");
+static_assert(kG == kPersistentGrid, "one launch counter per workgroup of a persistent launch");
 
-// Ticket of this workgroup (one thread asks; the caller broadcasts the tag it gives).
-__device__ __forceinline__ uint64_t take_ticket(uint8_t *head)
+// This workgroup's launch counter (one thread reads it; the caller broadcasts the tag and
+// writes the counter back plus one with bump_launches).
+__device__ __forceinline__ uint32_t read_launches(uint8_t *head)
 {
-    return __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(head + kHeadTicket), 1ull, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(reinterpret_cast<uint32_t *>(head + kHeadCounters) + blockIdx.x, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void bump_launches(uint8_t *head, uint32_t launches)
+{
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(head + kHeadCounters) + blockIdx.x, launches + 1u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t diag_word(const uint8_t *head)
 {
@@ -217,7 +225,7 @@ struct D1Args {
     int32_t *ids;
     float *tw;
     int32_t *counts, *offsets, *sa, *ap;  // null in a chain
-    uint8_t *head;   // workspace head: ticket counter, error flags, diagnostic switch
+    uint8_t *head;   // workspace head: launch counters, error flags, diagnostic switch
     uint64_t *xlog;  // [256] exchange words: logit of expert b (workgroup b)
     uint64_t *xh;    // [(k + S + 1) / 2][I] exchange words, two slots each: slot j < k = j-th
                      // selected expert, slot k = shared
@@ -304,12 +312,12 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
     const int rows_h = H / kG;                        // down rows (columns of y) per workgroup
     const int n0 = b * rows_h;
     const int i0 = b * I / kG, npair = (b + 1) * I / kG - i0;  // gate/up rows of every expert
-    // The ticket is asked for before anything else; wave 0 needs its tag only once its router
-    // row is in (its loads return in order), the other waves read it from LDS after phase 1.
-    uint64_t ticket = 0;
-    uint32_t diag = 0;
+    // The launch counter is read before anything else; wave 0 needs the tag only once its
+    // router row is in (its loads return in order), the other waves read it from LDS after
+    // phase 1.
+    uint32_t launches = 0, diag = 0;
     if (tid == 0) {
-        ticket = take_ticket(a.head);
+        launches = read_launches(a.head);
         diag = diag_word(a.head);
     }
     const size_t drow_bytes = FMT == 0 ? (size_t)I * 2 : (size_t)I / 2 + scale_row_bytes(FMT, I);
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         if (S) load_down(k, E, 0, kWaves);
     }
     if (wave == 0) {
-        const uint32_t tag0 = __builtin_amdgcn_readlane(launch_tag(ticket), 0);
+        const uint32_t tag0 = __builtin_amdgcn_readlane(launch_tag(launches), 0);
         if (lane == 0) {
             sh.tag = tag0;
             sh.giveup = diag;
@@ -626,6 +634,9 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
         if (a.xnext)
             a.xnext[n0 + n] = (uint16_t)(a.residual ? f2bf(bf2f(a.x[n0 + n]) + bf2f(yv)) : yv);
     }
+    // last: a write-through store in flight holds up the next barrier's wait (measured
+    // 1.2 us per layer when this store went out in phase 1)
+    if (tid == 0) bump_launches(a.head, launches);
 }
 
 // ---------------------------------------------------------------- dense layer, one token
@@ -640,7 +651,7 @@ __global__ __launch_bounds__(512) void decode1_kernel(D1Args a)
 //               the rows' codes, then their scales), and take no part in polling (a
 //               wave's loads return in order).
 //   all         down row n = wave of the slice against h from LDS -> y.
-// The launch tag comes from the workgroup's ticket, as in decode1_kernel.
+// The launch tag comes from the workgroup's launch counter, as in decode1_kernel.
 constexpr int kDenseRowWaves = 8, kDenseWaves = kDenseRowWaves + 4, kDenseMaxI = 4096;
 
 template <int FMT>
@@ -659,10 +670,9 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
     // for no load, so the gate/up rows, on which h and the exchange wait, are ahead of the
     // down rows in the memory queues and the down rows land while h is exchanged.
     const bool rows = wave < kDenseRowWaves && wave < nq;
-    uint64_t ticket = 0;  // asked for first; needed only once the rows' products are done
-    uint32_t diag = 0;
+    uint32_t launches = 0, diag = 0;  // read first; needed only once the rows' products are done
     if (tid == 0) {
-        ticket = take_ticket(a.head);
+        launches = read_launches(a.head);
         diag = diag_word(a.head);
     }
     const int i = 2 * (q0 + wave);
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
     // The tag reaches every wave through LDS behind a barrier that waits for LDS writes
     // only (the copy waves' copies stay in flight).
     if (tid == 0) {
-        s_tag[0] = launch_tag(ticket);
+        s_tag[0] = launch_tag(launches);
         s_tag[1] = diag;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
@@ -761,6 +771,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void dense1_kernel(D1Args a)
         if (FMT == 1) acc *= *a.w.down.ts_shared;
         if (lane == 0) a.y[n0 + wave] = (uint16_t)f2bf(acc);
     }
+    if (tid == 0) bump_launches(a.head, launches);  // last, as in decode1_kernel
 }
 
 }  // namespace
