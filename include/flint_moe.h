@@ -37,14 +37,16 @@
  *     their scales must be NULL); flint_moe_route and flint_moe_permute return
  *     FLINT_ERR_SHAPE.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
- *   - A workspace's first 96 KiB (the head) hold the persistent launches' ticket counter,
+ *   - A workspace's first 96 KiB (the head) hold the persistent launches' launch counters,
  *     the error flags, the small-batch arrival counter and exchange words: zero them once
  *     before first use (flint_moe_workspace_init, or any zero fill) and leave them to the
- *     library afterwards.  Head words: u64 at byte 0 = ticket counter; u32 at byte 8 =
- *     error flags (read and cleared by flint_moe_workspace_status); u32 at byte 12 = the
- *     small-batch arrival counter; u32 at byte 16 = a diagnostic switch, 0 in normal use:
- *     nonzero makes every bounded wait of the persistent launches give up at once (it
- *     exists so that the timeout report can be tested; results are then unreliable).
+ *     library afterwards.  Head words: u32 at byte 8 = error flags (read and cleared by
+ *     flint_moe_workspace_status); u32 at byte 12 = the small-batch arrival counter; u32 at
+ *     byte 16 = a diagnostic switch, 0 in normal use: nonzero makes every bounded wait of
+ *     the persistent launches give up at once (it exists so that the timeout report can be
+ *     tested; results are then unreliable); u32 [256] at byte 1024 = launch counters, each
+ *     the number of persistent launches (single-token layer launches) made on the
+ *     workspace so far.
  */
 #ifndef FLINT_MOE_H
 #define FLINT_MOE_H

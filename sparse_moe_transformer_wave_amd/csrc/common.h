@@ -97,22 +97,24 @@ hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, co
                                 int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap,
                                 const Plan &plan, int *arrivals, hipStream_t st);
 // Workspace head: the first kSyncBytes of every workspace (zeroed once before first use).
-//   u64 at kHeadTicket    ticket counter: every workgroup of a persistent launch takes one
-//                         ticket (each such launch has exactly kPersistentGrid workgroups),
-//                         so ticket / kPersistentGrid numbers the launch and gives its tag
 //   u32 at kHeadError     error flags (FLINT_WS_WAIT_TIMEOUT); cleared by the status call
 //   u32 at kHeadArrivals  arrival counter of the small-batch router launch (re-armed by it)
 //   u32 at kHeadDiag      diagnostic switch: nonzero makes every bounded wait give up at once
+//   u32 [kPersistentGrid] at kHeadCounters  launch counters, one per workgroup index: every
+//                         persistent launch has exactly kPersistentGrid workgroups and
+//                         workgroup b adds one to counter b, so all counters hold the number
+//                         of persistent launches before the current one, which gives its tag
 //   exchange words of the persistent launches from kHeadXchg on
 constexpr size_t kSyncBytes = 96 * 1024;
-constexpr size_t kHeadTicket = 0, kHeadError = 8, kHeadArrivals = 12, kHeadDiag = 16, kHeadXchg = 1024;
+constexpr size_t kHeadError = 8, kHeadArrivals = 12, kHeadDiag = 16, kHeadCounters = 1024, kHeadXchg = 2048;
 constexpr int kPersistentGrid = 256;
 constexpr uint32_t kWsWaitTimeout = 1u;  // FLINT_WS_WAIT_TIMEOUT
-// Tag of a persistent launch from one of its tickets: 1 .. 2^32 - 1, never 0 (the value of a
-// zeroed exchange word), and different for consecutive launches.
-__host__ __device__ inline uint32_t launch_tag(uint64_t ticket)
+static_assert(kHeadCounters + 4 * kPersistentGrid <= kHeadXchg, "launch counters overlap the exchange words");
+// Tag of the persistent launch that follows `launches` earlier ones: 1 .. 2^32 - 1, never 0
+// (the value of a zeroed exchange word); it repeats only after 2^32 - 1 launches.
+__host__ __device__ inline uint32_t launch_tag(uint32_t launches)
 {
-    return (uint32_t)((ticket / kPersistentGrid) % 0xffffffffull) + 1u;
+    return launches % 0xffffffffu + 1u;
 }
 // Copies the head's error flags to *out and clears them (one thread).
 hipError_t launch_ws_status(void *head, int32_t *out, hipStream_t st);

@@ -21,10 +21,12 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _tickets(ws):
-    """The workspace head's ticket counter: every workgroup of a persistent launch (256 of
-    them) takes one ticket."""
-    return int(ws[fm.HEAD_TICKET:fm.HEAD_TICKET + 8].view(torch.int64).item())
+def _launches(ws):
+    """Persistent launches made on a workspace: the head holds one launch counter per
+    workgroup index (256 of them, all equal between launches)."""
+    c = ws[fm.HEAD_COUNTERS:fm.HEAD_COUNTERS + 4 * 256].view(torch.int32).cpu().numpy()
+    assert np.all(c == c[0]), "launch counters disagree"
+    return int(c[0])
 
 
 def _tile_edge_tokens(c, g, n_hot=4, bm=256):
@@ -197,8 +199,8 @@ def test_full_prefill_8192(zipf):
 def test_single_token_launch_reuses_workspace(fmt):
     """T = 1 runs as one persistent launch whose workgroups exchange logits and h through
     launch-tagged words at the start of the workspace: consecutive calls on one workspace
-    (each reading words the previous call tagged) all match the reference, the ticket
-    counter advances by 256 per call (one per workgroup) and no wait ever timed out."""
+    (each reading words the previous call tagged) all match the reference, the launch
+    counters advance by one per call and no wait ever timed out."""
     d = fm.desc(2048, 768)
     ws = fm.workspace(d, 1, fmt)
     for n_call, layer in enumerate((0, 1, 2, 3, 0)):
@@ -213,7 +215,7 @@ def test_single_token_launch_reuses_workspace(fmt):
         w64 = check_routing(c, g)
         rm, rl = check_forward(c, g, w64)
         assert fm.workspace_status(ws) == 0, "a wait timed out"
-        assert _tickets(ws) == 256 * (n_call + 1)
+        assert _launches(ws) == n_call + 1
         _say("layer %d fmt %d: max rel %.2e rel L1 %.2e" % (layer, fmt, rm, rl))
 
 
@@ -372,7 +374,7 @@ def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
         _say("  layer %d: max rel %.2e, rel L1 %.2e" % (l, rm, rl))
         xl = _next_token(xl, yg[l:l + 1], residual)
     assert fm.workspace_status(ws) == 0, "a wait timed out"
-    return ws, _tickets(ws)
+    return ws, _launches(ws)
 
 
 @pytest.mark.parametrize("residual", [False, True])
@@ -385,10 +387,10 @@ def test_chain_tiny(residual):
 
 def test_chain_tiny_two_launches_and_counter():
     """20 layers (the host gathers layer descriptors 16 at a time, so the token crosses
-    that boundary too); the ticket counter advances by 256 per layer, and a following
+    that boundary too); the launch counters advance by one per layer, and a following
     single-token layer call on the same workspace is still correct."""
-    ws, tickets = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 20, True)
-    assert tickets == 20 * 256, tickets
+    ws, launches = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 20, True)
+    assert launches == 20, launches
     c = Case(1, 256, 128, 256, 6, layer=3).upload()
     out = c.alloc_out()
     routing = {kk: out[kk] for kk in ("logits", "topk_ids", "topk_w", "counts", "offsets",
@@ -398,7 +400,7 @@ def test_chain_tiny_two_launches_and_counter():
     from moe_cases import to_host
     g = to_host(out, c)
     check_forward(c, g, check_routing(c, g))
-    assert _tickets(ws) == 21 * 256 and fm.workspace_status(ws) == 0
+    assert _launches(ws) == 21 and fm.workspace_status(ws) == 0
 
 
 def test_chain_tiny_nvfp4():
