@@ -241,14 +241,24 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
     }
 }
 
-// Small batches (2 <= T <= 32): router and routing in one launch.  Workgroup e (16 waves,
-// wave w takes tokens w and w + 16) computes the logits of expert e and writes them with
-// agent-scope write-through stores; once they have completed it counts itself in at an
-// agent-scope arrival counter.  The workgroup that arrives last has every logit: it reads
-// them back with agent-scope loads into LDS, selects the top-k of every token (one token
-// per wave; four per wave measured slower at 32 tokens), groups the assignments by expert
-// and writes the plan, so the expert kernels that follow need no routing step of their own.
-// It also re-arms the counter.
+// Small batches (T <= 32, unless the single-token launch takes T = 1): router and routing in
+// one launch.  Workgroup e (16 waves, wave w takes tokens w and w + 16) computes the logits
+// of expert e and writes them with agent-scope write-through stores; once they have
+// completed it counts itself in at an agent-scope arrival counter.  The workgroup that
+// arrives last has every logit: it reads them back with agent-scope loads into LDS, selects
+// the top-k of every token (one token per wave; four per wave measured slower at 32
+// tokens), groups the assignments by expert and writes the plan, so the expert kernels that
+// follow need no routing step of their own.  It also re-arms the counter.
+//
+// The hand-off uses relaxed atomics, not release/acquire, and rests on how gfx950 carries
+// out agent-scope atomics: an agent-scope store is written through to the memory side,
+// which every XCD sees (global_store ... sc1), s_waitcnt vmcnt(0) returns only once the
+// memory side has acknowledged it, and an agent-scope load (sc1) reads the memory side, not
+// a stale L2 line.  So every logit store has reached the memory side before its
+// workgroup's counter increment is issued, and the last workgroup's loads are issued after
+// that increment returned.  A release/acquire pair at agent scope would add an L2
+// write-back and invalidate in every workgroup (buffer_wbl2 / buffer_inv sc1), which
+// measured far slower than this launch's whole selection.
 __global__ __launch_bounds__(1024) void router_select_kernel(
     int T, int H, int E, int k, int S, int renorm, const uint16_t *__restrict__ x,
     const float *__restrict__ Wr, const float *__restrict__ bias, float *__restrict__ logits,
