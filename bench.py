@@ -19,7 +19,8 @@ constant and SHA-256 digests of the input tokens and of the last layer's output.
 
 Other workloads through --configs: int4_t1/8/32, nvfp4_prefill, int4_prefill, dense_t1/t32/
 prefill (the dense SwiGLU layer, no router, I = 4096), nvfp4_dense_t1, int4_dense_t1, and
-chain_t1 / nvfp4_chain_t1 (one flint_moe_decode_chain call per step through the 47 layers).
+chain_t1 / nvfp4_chain_t1 / chain_t8 / nvfp4_chain_t8 (one flint_moe_decode_chain call per step
+through the 47 layers, 1 or 8 tokens).
 
 The timed trials of each workload sit between two flint_moe_workspace_status calls, whose
 one-thread kernel (ws_status_kernel) marks them in a rocprofv3 kernel trace or counter
@@ -62,6 +63,9 @@ CONFIGS = {
     # bf16(previous token + previous layer's output) formed by the previous layer's kernel
     "chain_t1": dict(T=1, fmt=0, layers=47, zipf=False, chain=True),
     "nvfp4_chain_t1": dict(T=1, fmt=1, layers=47, zipf=False, chain=True),
+    # eight tokens through the 47 layers the same way
+    "chain_t8": dict(T=8, fmt=0, layers=47, zipf=False, chain=True),
+    "nvfp4_chain_t8": dict(T=8, fmt=1, layers=47, zipf=False, chain=True),
     # dense SwiGLU layers (E = 0, k = 0, the shared expert alone; 16 distinct layers cycled)
     "dense_t1": dict(T=1, fmt=0, layers=16, zipf=False, dense=True),
     "dense_t32": dict(T=32, fmt=0, layers=16, zipf=False, dense=True),
@@ -347,21 +351,26 @@ def run_config(name, args, torch, fm, dg, pools):
     # Routing of every layer (for the algorithmic bytes: distinct experts touched), outside
     # the timed region.
     touched = []
+    ychain = None
+    L_lib = fm.lib()
+    if chain:
+        ychain = torch.empty((L, T, H_), dtype=torch.int16, device="cuda")
+        refs = fm.layer_refs([(d["weights"], d["Wr"], d["bias"]) for d in layers])
     if E_ and not chain:
         counts = torch.zeros(E_, dtype=torch.int32, device="cuda")
         for d in layers:
             fm.layer(desc, d["weights"], T, x, d["Wr"], d["bias"], y, ws, {"counts": counts})
             touched.append(int((counts > 0).sum().item()))
+    elif chain and T > 1:  # each layer's routing from one untimed pass of the chain
+        ids = torch.zeros((L, T, k_), dtype=torch.int32, device="cuda")
+        fm.decode_chain(desc, [(d["weights"], d["Wr"], d["bias"]) for d in layers], x, ychain, ws,
+                        topk_ids=ids, residual=True)
+        touched = [len(set(r.reshape(-1).tolist())) for r in ids.cpu().numpy()]
     else:
         touched = [TOPK if E_ else 0] * L  # a single token touches exactly k routed experts
     xb = expert_bytes(fmt, H_, I_)
     alg_bytes = [(u + S_) * xb + E_ * H_ * 4 + 4 * T * H_ for u in touched]
     flops_layer = 2.0 * T * (k_ + S_) * 3 * H_ * I_
-    ychain = None
-    L_lib = fm.lib()
-    if chain:
-        ychain = torch.empty((L, H_), dtype=torch.int16, device="cuda")
-        refs = fm.layer_refs([(d["weights"], d["Wr"], d["bias"]) for d in layers])
 
     def capture(n_steps):
         g = torch.cuda.CUDAGraph()
@@ -369,7 +378,7 @@ def run_config(name, args, torch, fm, dg, pools):
             st = torch.cuda.current_stream().cuda_stream
             if chain:
                 fn, fname = L_lib.flint_moe_decode_chain, "flint_moe_decode_chain"
-                calls = [((ctypes.byref(desc), refs, L, fm.CHAIN_RESIDUAL, x.data_ptr(), ychain.data_ptr(),
+                calls = [((ctypes.byref(desc), refs, L, fm.CHAIN_RESIDUAL, T, x.data_ptr(), ychain.data_ptr(),
                            None, None, None, ws.data_ptr(), ws.numel(), st), refs)]
             else:
                 fn, fname = L_lib.flint_moe_layer, "flint_moe_layer"
@@ -424,8 +433,10 @@ def run_config(name, args, torch, fm, dg, pools):
         achieved = bytes_per_call / (layer_ms / 1e3) / 1e9
         kernel = ("dense1_kernel (the whole dense layer in one persistent launch)" if E_ == 0 and T == 1 else
                   "the dense layer's gate/up and down kernels" if E_ == 0 else
-                  "decode1_kernel (one persistent launch per layer; chain time / layers)" if chain else
+                  "decode1_kernel (one persistent launch per layer; chain time / layers)" if chain and T == 1 else
+                  "decode_few_kernel (one persistent launch per layer; chain time / layers)" if chain else
                   "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
+                  "decode_few_kernel (the whole layer in one persistent launch)" if T <= 16 else
                   "one layer call: router with selection, gate/up, down and combine kernels")
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
@@ -440,7 +451,7 @@ def run_config(name, args, torch, fm, dg, pools):
                            "avg_launch_us": round(layer_ms * 1e3, 2), "alg_flops_per_launch": flops_layer,
                            "alg_bytes_per_launch": int(sum(alg_bytes) / L),
                            "hbm_floor_us": round(sum(alg_bytes) / L / (HBM_PEAK_GBS * 1e9) * 1e6, 1)}
-    out["sha256"] = {"x": sha256_of(x), "y_last_layer": sha256_of(ychain[-1:] if chain else y)}
+    out["sha256"] = {"x": sha256_of(x), "y_last_layer": sha256_of(ychain[-1] if chain else y)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(torch, cfg, layers, x.cpu().numpy().view("uint16"), args.cpu_seconds)
     log("  %s: %.1f tokens/s, %.2f us per layer (IQR %.4f ms over %d trials), %s %.3f of peak"

@@ -37,7 +37,7 @@
  *     their scales must be NULL); flint_moe_route and flint_moe_permute return
  *     FLINT_ERR_SHAPE.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
- *   - A workspace's first 96 KiB (the head) hold the persistent launches' launch counters,
+ *   - A workspace's first 4 MiB (the head) hold the persistent launches' launch counters,
  *     the error flags, the small-batch arrival counter and exchange words: zero them once
  *     before first use (flint_moe_workspace_init, or any zero fill) and leave them to the
  *     library afterwards.  Head words: u32 at byte 8 = error flags (read and cleared by
@@ -45,8 +45,8 @@
  *     byte 16 = a diagnostic switch, 0 in normal use: nonzero makes every bounded wait of
  *     the persistent launches give up at once (it exists so that the timeout report can be
  *     tested; results are then unreliable); u32 [256] at byte 1024 = launch counters, each
- *     the number of persistent launches (single-token layer launches) made on the
- *     workspace so far.
+ *     the number of persistent launches (single-token and small-batch layer launches) made
+ *     on the workspace so far.
  */
 #ifndef FLINT_MOE_H
 #define FLINT_MOE_H
@@ -152,14 +152,14 @@ typedef struct {
    given weight format.  Returns 0 for an invalid descriptor or T_max < 0. */
 size_t flint_moe_workspace_bytes(const flint_moe_desc *desc, int64_t T_max, int32_t format);
 
-/* Zero the first 96 KiB of a workspace (a small fill kernel on `stream`; no
+/* Zero the first 4 MiB of a workspace (a small fill kernel on `stream`; no
    allocation).  Call once per workspace before its first use. */
 int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* The error flags (FLINT_WS_*) that calls on this workspace have raised since the last
    status call, written to *flags (a device int32, 4-byte aligned) by a one-thread kernel on
    `stream`, which also clears them; queue it after the calls to check, and read *flags once
-   the stream has reached it.  0 = no error.  ws_bytes >= 96 KiB. */
+   the stream has reached it.  0 = no error.  ws_bytes >= 4 MiB. */
 int flint_moe_workspace_status(void *ws, size_t ws_bytes, int32_t *flags, void *stream);
 
 /* Static text for a status code; for FLINT_ERR_HIP it also names the last HIP error
@@ -244,7 +244,7 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
    the workspace head described above, never cleared by a call; its error flags are not
    reported (use flint_moe_layer with a workspace of your own to read them).
    Returns FLINT_ERR_WORKSPACE when flint_moe_workspace_bytes(desc, T, format) exceeds
-   16 MiB (at H = 2048, I = 768, E = 256, k = 6 with a shared expert: T above about 200);
+   16 MiB (at H = 2048, I = 768, E = 256, k = 6 with a shared expert: T above 157);
    otherwise exactly as flint_moe_layer. */
 int flint_moe_layer_noalloc(const flint_moe_desc *desc, const flint_moe_weights *weights, int64_t T,
                             const uint16_t *x, const float *w_router, const float *logit_bias,
@@ -263,27 +263,30 @@ enum {
     FLINT_CHAIN_RESIDUAL = 1  /* the next layer's token is bf16(x_l + y_l) instead of y_l */
 };
 
-/* A single token through n_layers MoE layers, one after the other, in few launches:
-     x_0 = x;  y_l = layer_l(x_l) exactly as flint_moe_layer computes it for T = 1;
+/* A decode batch of T tokens (1 <= T <= 16) through n_layers MoE layers, one after the
+   other, one persistent launch per layer:
+     x_0 = x;  y_l = layer_l(x_l) exactly as flint_moe_layer computes it for T tokens;
      x_{l+1} = y_l, or bf16(x_l + y_l) (one fp32 sum, rounded once) with FLINT_CHAIN_RESIDUAL.
    The pages' GB200 runtime has a low-latency decode path for up to 8 requests and the
    Apple runtime a Metal megakernel (recipes.vllm.ai "RecursiveSI/flint", Overview;
-   mrchatgpt.org explainer, section 4, the item on kernels).  Here every layer is the
-   single-token persistent launch of flint_moe_layer; its last phase also forms the next
-   layer's token and leaves it in the workspace head for the next launch, so the chain
-   costs no work between layers.  (Running several layers inside one launch, trading the
-   token through tagged words, was measured slower on this GPU: the layer loop costs the
-   kernel registers that its single-layer form keeps for loads in flight.)
+   mrchatgpt.org explainer, section 4, the item on kernels).  Every layer is the persistent
+   launch flint_moe_layer uses for T tokens (T = 1: the single-token launch; 2 <= T <= 16:
+   the small-batch launch); its last phase also forms the next layer's tokens and leaves
+   them in the workspace head for the next launch, so the chain costs no work between
+   layers.  (Running several layers inside one launch, trading the tokens through tagged
+   words, was measured slower on this GPU: the layer loop costs the kernel registers that
+   its single-layer form keeps for loads in flight.)
    layers: host array [n_layers] (read during the call only).  All layers share `desc` and
-   one weight format.  x: bf16 [H]; y: bf16 [n_layers][H], every layer's output y_l;
-   topk_ids / topk_w: [n_layers][k] or NULL; logits: [n_layers][E] fp32 or NULL.  Needs the
-   single-token persistent path: E >= 1, hidden % 256 == 0 and hidden <= 2048,
-   inter <= 1024, k <= 8, the down rows of one 1/256 slice of hidden in whole 16-byte
-   chunks, and a device with at least 256 CUs where one workgroup fits on a CU
-   (FLINT_ERR_SHAPE otherwise).  ws: at least flint_moe_workspace_bytes(desc, 1, format)
-   bytes, initialised once (flint_moe_workspace_init).  0 <= n_layers <= 4096. */
+   one weight format.  x: bf16 [T][H]; y: bf16 [n_layers][T][H], every layer's output y_l;
+   topk_ids / topk_w: [n_layers][T][k] or NULL; logits: [n_layers][T][E] fp32 or NULL.
+   Needs the persistent launch for T: E >= 1, k <= 8, a device with at least 256 CUs where
+   one workgroup fits on a CU, and for T = 1 hidden % 256 == 0, hidden <= 2048,
+   inter <= 1024 and the down rows of one 1/256 slice of hidden in whole 16-byte chunks; for
+   T >= 2 hidden <= 2048, inter <= 1024 and E <= 256 (FLINT_ERR_SHAPE otherwise, also for T
+   outside 1..16).  ws: at least flint_moe_workspace_bytes(desc, T, format) bytes,
+   initialised once (flint_moe_workspace_init).  0 <= n_layers <= 4096. */
 int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref *layers,
-                           int32_t n_layers, uint32_t flags, const uint16_t *x, uint16_t *y,
+                           int32_t n_layers, uint32_t flags, int64_t T, const uint16_t *x, uint16_t *y,
                            int32_t *topk_ids, float *topk_w, float *logits, void *ws,
                            size_t ws_bytes, void *stream);
 

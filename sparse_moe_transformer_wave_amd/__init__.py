@@ -92,8 +92,8 @@ def lib():
         L.flint_moe_forward.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.flint_moe_layer.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.flint_moe_layer_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp]
-        L.flint_moe_decode_chain.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_uint32, vp, vp, vp, vp,
-                                             vp, vp, sz, vp]
+        L.flint_moe_decode_chain.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64, vp, vp,
+                                             vp, vp, vp, vp, sz, vp]
         for f in ("flint_moe_route", "flint_moe_permute", "flint_moe_forward", "flint_moe_layer",
                   "flint_moe_decode_chain", "flint_moe_layer_noalloc"):
             getattr(L, f).restype = ctypes.c_int
@@ -254,11 +254,12 @@ def layer_refs(layers):
 
 def decode_chain(d: Desc, layers, x, y, ws, topk_ids=None, topk_w=None, logits=None,
                  residual=False, stream=None):
-    """One token through len(layers) layers (flint_moe_decode_chain); layers = list of
-    (Weights, w_router, logit_bias); y: [L][H] bf16 (int16 tensor)."""
+    """T = x.numel() / hidden tokens through len(layers) layers (flint_moe_decode_chain);
+    layers = list of (Weights, w_router, logit_bias); y: [L][T][H] bf16 (int16 tensor)."""
     refs = layer_refs(layers)
+    T = x.numel() // d.hidden
     rc = lib().flint_moe_decode_chain(ctypes.byref(d), refs, len(layers),
-                                      CHAIN_RESIDUAL if residual else 0, _ptr(x), _ptr(y),
+                                      CHAIN_RESIDUAL if residual else 0, T, _ptr(x), _ptr(y),
                                       _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(ws), _nbytes(ws),
                                       _stream(stream))
     _check(rc, "flint_moe_decode_chain")

@@ -427,6 +427,12 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
         return hip_status(launch_decode1(s, wset_of(weights), x, w_router, logit_bias, y, lg, ids, tw,
                                          cnt, off, sa, ap, b + L.sync, st));
     }
+    // The small-batch launch for bf16 weights; with 4-bit weights the dequantisation makes its
+    // streaming waves VALU-bound and the four-launch path below measured faster per layer.
+    if (weights->format == FLINT_WFMT_BF16 && decode_few_supported(s, weights->format, T)) {
+        return hip_status(launch_decode_few(s, wset_of(weights), T, x, w_router, logit_bias, y, lg, ids, tw,
+                                            cnt, off, sa, ap, b + L.sync, st));
+    }
     if (T <= kGemvMaxT) {
         rc = hip_status(launch_router_select(s, T, x, w_router, logit_bias, lg, ids, tw, cnt, off,
                                              sa, ap, plan, (int *)(b + L.sync + kHeadArrivals), st));
@@ -444,13 +450,14 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
 }
 
 int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref *layers,
-                           int32_t n_layers, uint32_t flags, const uint16_t *x, uint16_t *y,
+                           int32_t n_layers, uint32_t flags, int64_t T, const uint16_t *x, uint16_t *y,
                            int32_t *topk_ids, float *topk_w, float *logits, void *ws,
                            size_t ws_bytes, void *stream)
 {
     int rc = check_desc(desc);
     if (rc) return rc;
     if (desc->n_experts == 0 || n_layers < 0 || n_layers > kMaxChainLayers) return FLINT_ERR_SHAPE;
+    if (T < 1 || T > kChainMaxT) return FLINT_ERR_SHAPE;
     if (flags & ~(uint32_t)FLINT_CHAIN_RESIDUAL) return FLINT_ERR_FORMAT;
     if (n_layers == 0) return FLINT_OK;
     if (!layers || !x || !y || !ws) return FLINT_ERR_NULL;
@@ -466,9 +473,11 @@ int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref
         if (!aligned16(layers[l].w_router) || !aligned16(layers[l].logit_bias)) return FLINT_ERR_ALIGN;
     }
     const Shape s = shape_of(desc);
-    if (ws_bytes < ws_layout(s, 1).total) return FLINT_ERR_WORKSPACE;
-    if (!decode1_supported(s, fmt)) return FLINT_ERR_SHAPE;
+    const WsLayout L = ws_layout(s, T);
+    if (ws_bytes < L.total) return FLINT_ERR_WORKSPACE;
+    if (T == 1 ? !decode1_supported(s, fmt) : !decode_few_supported(s, fmt, T)) return FLINT_ERR_SHAPE;
     hipStream_t st = (hipStream_t)stream;
+    char *b = (char *)ws;
     for (int l0 = 0; l0 < n_layers; l0 += kChainChunk) {
         const int n = n_layers - l0 < kChainChunk ? n_layers - l0 : kChainChunk;
         WSet w[kChainChunk];
@@ -478,11 +487,17 @@ int flint_moe_decode_chain(const flint_moe_desc *desc, const flint_moe_layer_ref
             wr[i] = layers[l0 + i].w_router;
             bias[i] = layers[l0 + i].logit_bias;
         }
-        rc = hip_status(launch_decode_chain(
-            s, w, wr, bias, n, flags & FLINT_CHAIN_RESIDUAL, l0 == 0 ? x : nullptr, l0 + n < n_layers,
-            y + (size_t)l0 * s.H, topk_ids ? topk_ids + (size_t)l0 * s.k : nullptr,
-            topk_w ? topk_w + (size_t)l0 * s.k : nullptr, logits ? logits + (size_t)l0 * s.E : nullptr,
-            ws, st));
+        const bool residual = flags & FLINT_CHAIN_RESIDUAL, hand_on = l0 + n < n_layers;
+        int32_t *ids = topk_ids ? topk_ids + (size_t)l0 * T * s.k : nullptr;
+        float *tw = topk_w ? topk_w + (size_t)l0 * T * s.k : nullptr;
+        float *lg = logits ? logits + (size_t)l0 * T * s.E : nullptr;
+        if (T == 1)
+            rc = hip_status(launch_decode_chain(s, w, wr, bias, n, residual, l0 == 0 ? x : nullptr, hand_on,
+                                                y + (size_t)l0 * s.H, ids, tw, lg, ws, st));
+        else
+            rc = hip_status(launch_decode_few_chain(s, w, wr, bias, n, l0, residual, T, x, hand_on,
+                                                    y + (size_t)l0 * T * s.H, ids, tw, lg, (int32_t *)(b + L.ids),
+                                                    (float *)(b + L.w), ws, st));
         if (rc) return rc;
     }
     return FLINT_OK;

@@ -104,8 +104,9 @@ hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, co
 //                         persistent launch has exactly kPersistentGrid workgroups and
 //                         workgroup b adds one to counter b, so all counters hold the number
 //                         of persistent launches before the current one, which gives its tag
-//   exchange words of the persistent launches from kHeadXchg on
-constexpr size_t kSyncBytes = 96 * 1024;
+//   exchange words of the persistent launches from kHeadXchg on: the single-token layers'
+//   up to kHeadFewXchg, the small-batch layer's from there (4 MiB in all)
+constexpr size_t kSyncBytes = 4096 * 1024, kHeadFewXchg = 96 * 1024;
 constexpr size_t kHeadError = 8, kHeadArrivals = 12, kHeadDiag = 16, kHeadCounters = 1024, kHeadXchg = 2048;
 constexpr int kPersistentGrid = 256;
 constexpr uint32_t kWsWaitTimeout = 1u;  // FLINT_WS_WAIT_TIMEOUT
@@ -129,6 +130,24 @@ hipError_t launch_decode1(const Shape &s, const WSet &w, const uint16_t *x, cons
 // Dense SwiGLU layer (E = 0, the one expert held as the shared expert), one token in any
 // weight format, in one persistent launch (decode1.hip); same head and CU check as
 // launch_decode1.
+// A small decode batch (2 <= T <= 16) in one persistent launch (decode_few.hip); the same
+// residency checks as decode1_supported.
+bool decode_few_supported(const Shape &s, int fmt, int64_t T);
+hipError_t launch_decode_few(const Shape &s, const WSet &w, int64_t T, const uint16_t *x, const float *Wr,
+                             const float *bias, uint16_t *y, float *logits, int32_t *ids, float *tw,
+                             int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap, void *head,
+                             hipStream_t st);
+// A small batch through L layers (decode_few.hip), layer l0 + l of the whole chain at
+// position l: its tokens come from x (the chain's first layer) or the head's token buffer
+// (l0 + l) % 2, its next layer's go to the other buffer; `hand_on` as in
+// launch_decode_chain.  ids / tw may be null: the routing then goes to the scratch arrays
+// (T k each).  y: [L][T][H]; ids, tw: [L][T][k]; logits: [L][T][E] or null.
+hipError_t launch_decode_few_chain(const Shape &s, const WSet *w, const float *const *Wr,
+                                   const float *const *bias, int L, int l0, bool residual, int64_t T,
+                                   const uint16_t *x, bool hand_on, uint16_t *y, int32_t *ids, float *tw,
+                                   float *logits, int32_t *ids_scratch, float *tw_scratch, void *head,
+                                   hipStream_t st);
+constexpr int kChainMaxT = 16;  // tokens of a decode chain: 1 (single-token launch) or 2 .. 16
 bool dense1_supported(const Shape &s, int fmt);
 hipError_t launch_dense1(const Shape &s, const WSet &w, const uint16_t *x, uint16_t *y, void *head,
                          hipStream_t st);

@@ -38,7 +38,7 @@
 // cleared by flint_moe_workspace_status) and carries on with the values it has.  All 256
 // workgroups must be resident together (one per CU): the host checks the CU count and the
 // kernel's occupancy before choosing this launch.
-#include "common.h"
+#include "xchg.h"
 
 #include <map>
 #include <mutex>
@@ -52,7 +52,6 @@ constexpr int kG = 256;        // workgroups (one per CU)
 constexpr int kWaves = 8;
 constexpr int kMaxK = 8;
 constexpr int kMaxXC = 4;      // 16-byte x chunks per lane: H <= 2048
-constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
 
 // Exchange words in the workspace head (see common.h for the head's control words): u64
 // words for the logits at kXLogOff (one per workgroup: the fp32 logit) and for h at kXHOff
@@ -63,26 +62,8 @@ constexpr int kSpin = 1 << 16; // bounded waits (each try is a ~1 us round trip)
 // buffer at kXNextOff.
 constexpr size_t kXLogOff = kHeadXchg, kXHOff = kXLogOff + 8 * kG;
 constexpr size_t kXNextOff = kXHOff + 8 * (size_t)(kMaxK + 1) * 1024;
-static_assert(kXNextOff + 2 * 2048 <= kSyncBytes, "exchange words exceed the head");
+static_assert(kXNextOff + 2 * 2048 <= kHeadFewXchg, "exchange words exceed their part of the head");
 static_assert(kG == kPersistentGrid, "one launch counter per workgroup of a persistent launch");
-
-// This workgroup's launch counter (one thread reads it; the caller broadcasts the tag and
-// writes the counter back plus one with bump_launches).
-__device__ __forceinline__ uint32_t read_launches(uint8_t *head)
-{
-    return __hip_atomic_load(reinterpret_cast<uint32_t *>(head + kHeadCounters) + blockIdx.x, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void bump_launches(uint8_t *head, uint32_t launches)
-{
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(head + kHeadCounters) + blockIdx.x, launches + 1u,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t diag_word(const uint8_t *head)
-{
-    return __hip_atomic_load(reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(head) + kHeadDiag),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -92,46 +73,6 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ void lds_load16(const void *g, uint8_t *lds)
 {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-__device__ __forceinline__ void put_word(uint64_t *p, uint32_t tag, float v)
-{
-    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// h of two slots at one row of I: bf16(lo) in bits 0-15, bf16(hi) in bits 16-31.
-__device__ __forceinline__ void put_h2(uint64_t *p, uint32_t tag, float lo, float hi)
-{
-    __hip_atomic_store(p, ((uint64_t)tag << 32) | f2bf(lo) | (f2bf(hi) << 16), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t get_word(const uint64_t *p)
-{
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Waits until the words w[q] (q < nq, read from p + stride * q) all carry `tag`.  The
-// missing ones are re-read together, so each try costs one round trip however many are
-// late.  Bounded: on timeout (at once when `giveup`, the head's diagnostic switch) the error
-// flag is set and the stale values are kept.
-template <int N>
-__device__ __forceinline__ void await_words(const uint64_t *p, int stride, int nq, uint64_t *w, uint32_t tag,
-                                            uint8_t *head, bool giveup)
-{
-    for (int n = 0;; n++) {
-        bool miss = false;
-#pragma unroll
-        for (int q = 0; q < N; q++) miss |= q < nq && (uint32_t)(w[q] >> 32) != tag;
-        if (!miss) break;
-        if (giveup || n >= kSpin) {
-            __hip_atomic_fetch_or(reinterpret_cast<uint32_t *>(head + kHeadError), kWsWaitTimeout, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int q = 0; q < N; q++)
-            if (q < nq && (uint32_t)(w[q] >> 32) != tag) w[q] = get_word(p + (size_t)stride * q);
-    }
 }
 
 // 8 bf16 products summed into acc.  The elements go through named scalars: a bit cast
@@ -788,7 +729,7 @@ static size_t d1_dyn_bytes(const Shape &s, int fmt)
 // hipOccupancyMaxActiveBlocksPerMultiprocessor).  Asked once per (device, kernel, LDS bytes).
 // It cannot see other work on the GPU: a launch that shares the CUs with other kernels may
 // find its waits running out, which the workspace's error flags report.
-static bool persistent_fits(const void *kernel, int threads, size_t dyn)
+bool persistent_fits(const void *kernel, int threads, size_t dyn)
 {
     static std::mutex mu;
     static std::map<std::tuple<int, const void *, size_t>, bool> known;

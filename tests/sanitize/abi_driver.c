@@ -102,9 +102,10 @@ int main(void)
     lr[1].weights = wn;
     lr[1].w_router = A;
     const size_t need1 = flint_moe_workspace_bytes(&d, 1, FLINT_WFMT_BF16);
-    expect(flint_moe_decode_chain(&d, lr, 2, 0, A, A, NULL, NULL, NULL, A, need1, NULL), FLINT_ERR_FORMAT, "chain formats");
-    expect(flint_moe_decode_chain(&d, lr, 5000, 0, A, A, NULL, NULL, NULL, A, need1, NULL), FLINT_ERR_SHAPE, "chain n");
-    expect(flint_moe_decode_chain(&d, lr, 1, 0, A, A, NULL, NULL, NULL, A, need1 - 1, NULL), FLINT_ERR_WORKSPACE, "chain ws");
+    expect(flint_moe_decode_chain(&d, lr, 2, 0, 1, A, A, NULL, NULL, NULL, A, need1, NULL), FLINT_ERR_FORMAT, "chain formats");
+    expect(flint_moe_decode_chain(&d, lr, 5000, 0, 1, A, A, NULL, NULL, NULL, A, need1, NULL), FLINT_ERR_SHAPE, "chain n");
+    expect(flint_moe_decode_chain(&d, lr, 1, 0, 17, A, A, NULL, NULL, NULL, A, need1, NULL), FLINT_ERR_SHAPE, "chain T");
+    expect(flint_moe_decode_chain(&d, lr, 1, 0, 1, A, A, NULL, NULL, NULL, A, need1 - 1, NULL), FLINT_ERR_WORKSPACE, "chain ws");
     /* workspace init / status */
     expect(flint_moe_workspace_init(MIS, need, NULL), FLINT_ERR_ALIGN, "init align");
     expect(flint_moe_workspace_init(A, 100, NULL), FLINT_ERR_WORKSPACE, "init size");

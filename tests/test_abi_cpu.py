@@ -146,16 +146,17 @@ def test_decode_chain_validation():
     d = fm.desc(2048, 768)
     need = fm.workspace_bytes(d, 1)
 
-    def chain(layers, n=None, flags=0, x=A, y=A, ids=None, tw=None, ws=A, nb=need, dd=d):
+    def chain(layers, n=None, flags=0, T=1, x=A, y=A, ids=None, tw=None, ws=A, nb=need, dd=d):
         refs = fm.layer_refs(layers)
         return L.flint_moe_decode_chain(ctypes.byref(dd), refs if layers else None,
-                                        len(layers) if n is None else n, flags, x, y, ids, tw,
+                                        len(layers) if n is None else n, flags, T, x, y, ids, tw,
                                         None, ws, nb, None)
 
     good = (fm.Weights(fm.WFMT_BF16, A, A, A, A, A, A), A, None)
     assert chain([], n=0) == fm.OK
     assert chain([good], n=-1) == fm.ERR_SHAPE
     assert chain([good], n=5000) == fm.ERR_SHAPE
+    assert chain([good], T=0) == fm.ERR_SHAPE and chain([good], T=17) == fm.ERR_SHAPE
     assert chain([good], dd=fm.desc(2048, 768, n_experts=0, top_k=0)) == fm.ERR_SHAPE
     assert chain([good], flags=2) == fm.ERR_FORMAT
     assert chain([], n=1) == fm.ERR_NULL
@@ -231,6 +232,6 @@ def test_layer_noalloc_validation():
     assert call(-1) == fm.ERR_SHAPE
     assert call(4, wr=None) == fm.ERR_NULL
     assert call(4, y=MIS) == fm.ERR_ALIGN
-    assert fm.workspace_bytes(d, 180) <= 16 << 20 < fm.workspace_bytes(d, 256)
+    assert fm.workspace_bytes(d, 150) <= 16 << 20 < fm.workspace_bytes(d, 256)
     assert call(256) == fm.ERR_WORKSPACE
     assert call(65536) == fm.ERR_WORKSPACE

@@ -334,12 +334,12 @@ def _next_token(x_bits, y_bits, residual):
     return dg.f32_to_bf16_bits(s.astype(np.float32))
 
 
-def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
-    """flint_moe_decode_chain over L layers, each layer checked against the reference on
-    the token the GPU fed it (recomputed on the host from the GPU's y of the previous
-    layer), with the two-stage protocol of a single-token layer."""
-    _say("chain H=%d I=%d E=%d k=%d fmt=%d L=%d residual=%d" % (H, I, E, k, fmt, L, residual))
-    x0 = dg.normal_bf16((1, H), 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
+def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None, T=1):
+    """flint_moe_decode_chain over L layers for T tokens, each layer checked against the
+    reference on the tokens the GPU fed it (recomputed on the host from the GPU's y of the
+    previous layer), with the two-stage protocol of a layer call."""
+    _say("chain T=%d H=%d I=%d E=%d k=%d fmt=%d L=%d residual=%d" % (T, H, I, E, k, fmt, L, residual))
+    x0 = dg.normal_bf16((T, H), 0, dg.stream_id(0, dg.KIND_X, 0), dg.X_STD)
     cases = []
     xh = x0
     for l in range(L):
@@ -347,7 +347,7 @@ def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
         if predict_experts:  # the reference's own chain decides which experts get weights
             Wr = dg.normal_f32((E, H), 0, dg.stream_id(l, dg.KIND_ROUTER, 0), dg.ROUTER_STD)
             experts = sorted(set(oracle.select(oracle.router(xh, Wr), k).reshape(-1).tolist()))
-        c = Case(1, H, I, E, k, fmt=fmt, layer=l, experts=experts, x=xh).upload()
+        c = Case(T, H, I, E, k, fmt=fmt, layer=l, experts=experts, x=xh).upload()
         cases.append(c)
         if predict_experts and l + 1 < L:
             lg = oracle.router(xh, c.Wr)
@@ -355,11 +355,11 @@ def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
             yr = oracle.moe_tokens(c.routed, c.shared, xh, ids, oracle.weights(lg, ids, True))
             xh = _next_token(xh, dg.f32_to_bf16_bits(yr.astype(np.float32)), residual)
     d = cases[0].desc
-    y = torch.zeros((L, H), dtype=torch.int16, device="cuda")
-    ids = torch.zeros((L, k), dtype=torch.int32, device="cuda")
-    tw = torch.zeros((L, k), dtype=torch.float32, device="cuda")
-    lg = torch.zeros((L, E), dtype=torch.float32, device="cuda")
-    ws = fm.workspace(d, 1, fmt) if ws is None else ws
+    y = torch.zeros((L, T, H), dtype=torch.int16, device="cuda")
+    ids = torch.zeros((L, T, k), dtype=torch.int32, device="cuda")
+    tw = torch.zeros((L, T, k), dtype=torch.float32, device="cuda")
+    lg = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
+    ws = fm.workspace(d, T, fmt) if ws is None else ws
     fm.decode_chain(d, [(c.weights, c.d_Wr, None) for c in cases], cases[0].d_x, y, ws, ids, tw, lg,
                     residual=residual)
     torch.cuda.synchronize()
@@ -368,11 +368,11 @@ def _chain_check(H, I, E, k, fmt, L, residual, predict_experts=False, ws=None):
     xl = x0
     for l, c in enumerate(cases):
         c.x = xl  # the token the GPU fed layer l
-        g = {"logits": lgg[l:l + 1], "topk_ids": idg[l:l + 1], "topk_w": twg[l:l + 1], "y": yg[l:l + 1]}
+        g = {"logits": lgg[l], "topk_ids": idg[l], "topk_w": twg[l], "y": yg[l]}
         w64 = check_routing(c, g)
         rm, rl = check_forward(c, g, w64)
         _say("  layer %d: max rel %.2e, rel L1 %.2e" % (l, rm, rl))
-        xl = _next_token(xl, yg[l:l + 1], residual)
+        xl = _next_token(xl, yg[l], residual)
     assert fm.workspace_status(ws) == 0, "a wait timed out"
     return ws, _launches(ws)
 
@@ -442,6 +442,39 @@ def test_full_prefill_int4_8192():
 
 def test_chain_full_int4():
     _chain_check(2048, 768, 256, 6, fm.WFMT_INT4, 3, True, predict_experts=True)
+
+
+# ---------------------------------------------------------------- decode chains of a small batch
+@pytest.mark.parametrize("T,residual", [(8, True), (8, False), (16, True), (2, True)])
+def test_chain_batch_tiny(T, residual):
+    """A small batch through the layers: each layer is the small-batch launch, which forms
+    the next layer's tokens in its combine phase (two token buffers in the head, used in
+    turn); every layer checked on the tokens the GPU fed it."""
+    ws, launches = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 5 if residual else 4, residual, T=T)
+    assert launches == (5 if residual else 4)
+
+
+def test_chain_batch_crosses_the_descriptor_batches():
+    """18 layers (the host gathers descriptors 16 at a time: the token buffer of layer 16
+    comes from the previous batch's last launch), then a single-layer call on the same
+    workspace."""
+    ws, launches = _chain_check(256, 128, 256, 6, fm.WFMT_BF16, 18, True, T=8)
+    assert launches == 18
+    c = Case(8, 256, 128, 256, 6, layer=3).upload()
+    out = c.alloc_out()
+    fm.layer(c.desc, c.weights, 8, c.d_x, c.d_Wr, None, out["y"], ws,
+             {kk: out[kk] for kk in ("logits", "topk_ids", "topk_w", "counts", "offsets",
+                                     "sorted_assign", "assign_pos")})
+    torch.cuda.synchronize()
+    from moe_cases import to_host
+    g = to_host(out, c)
+    check_forward(c, g, check_routing(c, g))
+    assert _launches(ws) == 19 and fm.workspace_status(ws) == 0
+
+
+@pytest.mark.parametrize("fmt", [fm.WFMT_BF16, fm.WFMT_NVFP4, fm.WFMT_INT4])
+def test_chain_batch_full(fmt):
+    _chain_check(2048, 768, 256, 6, fmt, 3, True, predict_experts=True, T=8)
 
 
 # ---------------------------------------------------------------- HIP graph replay

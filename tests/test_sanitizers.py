@@ -31,7 +31,7 @@ def test_reference_under_asan_ubsan(tmp_path):
 @pytest.mark.skipif(not os.path.exists(CLANG), reason="ROCm clang not installed")
 def test_abi_validation_under_asan_ubsan(tmp_path):
     from sparse_moe_transformer_wave_amd import build as b
-    objs = [os.path.join(b.BUILD_DIR, "moe_%s.o" % n) for n in ("route", "permute", "gemv", "gemm", "decode1")]
+    objs = [os.path.join(b.BUILD_DIR, "moe_%s.o" % n) for n in ("route", "permute", "gemv", "gemm", "decode1", "decode_few")]
     if not all(os.path.exists(o) for o in objs):
         b.build_moe()
     api = str(tmp_path / "api_san.o")
