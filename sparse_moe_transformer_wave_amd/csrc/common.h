@@ -223,6 +223,22 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t q, float scale)
     if (scale == 0.f) r = u32x4{0u, 0u, 0u, 0u};
     return r;
 }
+// The same values with one select instead of four: a zero scale gives a zero mantissa
+// factor (the conversion itself then scales by 2^-127, still finite), so every product is
+// (signed) zero.  The streaming kernels use this form, which measured 1-4 % faster there;
+// the prefill GEMM keeps dequant8 (this form measured 8 % slower in it).
+__device__ __forceinline__ u32x4 dequant8_stream(uint32_t q, float scale)
+{
+    const float mant = scale == 0.f ? 0.f : __uint_as_float((__float_as_uint(scale) & 0x807fffffu) | 0x3f800000u);
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, scale, 3);
+    auto pack = [mant](f32x2 v) {
+        return __builtin_amdgcn_perm(__float_as_uint(v[1] * mant), __float_as_uint(v[0] * mant), 0x07060302u);
+    };
+    return u32x4{pack(v0), pack(v1), pack(v2), pack(v3)};
+}
 
 // INT4 (W4A16): signed nibble i of a word (two's complement, low nibble first) as an int.
 __device__ __forceinline__ int int4_at(uint32_t q, int i)

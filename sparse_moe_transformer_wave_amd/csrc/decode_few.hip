@@ -21,16 +21,18 @@
 //            A = all T tokens, whichever unit the block belongs to.  The tokens are the same
 //            for every expert (a token's rows for an expert it did not pick are computed and
 //            not stored), so the token fragments are loaded once per wave and the blocks of
-//            all units form one even list: workgroup b takes blocks [b n / 256, (b+1) n / 256).
+//            all units form one even list, dealt out round-robin (workgroup b takes blocks
+//            b, b + 256, ...).
 //            Seven waves split K; their partial tiles meet in LDS, where the eighth wave
 //            forms h = silu(g) u of the unit's tokens, rounded to bf16, and writes it out as
 //            words of two values.  (The streaming waves issue no stores: a wave's memory
 //            operations complete in order, so a write-through store would delay the wait
 //            for the next weight load by the store's round trip, once per block.)
-//   down     the units' 16-row blocks of H, divided the same way.  A = the unit's h rows
-//            (polled: a unit's words come from the few workgroups that own its gate/up
-//            blocks), B = 16 down rows; the eighth wave writes the per-slot outputs as fp32
-//            words.
+//   down     the units' 16-row blocks of H in contiguous ranges (workgroup b takes blocks
+//            [b n / 256, (b+1) n / 256), mostly of one unit).  A = the unit's h rows
+//            (polled; with the gate/up blocks dealt round-robin a unit's h is written by
+//            many workgroups, most units' long before the down phase), B = 16 down rows;
+//            the eighth wave writes the per-slot outputs as fp32 words.
 //   combine  workgroup b owns elements [b T H / 256, (b+1) T H / 256) of y: it polls the
 //            k + 1 slot words of each and sums them in fp32, shared first, then j
 //            ascending (news.ditty.ir, third paragraph: one shared expert always active).
@@ -139,10 +141,10 @@ __device__ __forceinline__ f32x4 tile_mma(const u32x4 *a, const u32x4 *v, const 
                 const u32x4 q = v[c];
                 const uint32_t q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
                 const float s0 = e4m3_to_f32(sc[c] & 0xffu), s1 = e4m3_to_f32((sc[c] >> 8) & 0xffu);
-                acc = mfma16x16x32(as_bf16x8(a[4 * c]), as_bf16x8(dequant8(q0, s0)), acc);
-                acc = mfma16x16x32(as_bf16x8(a[4 * c + 1]), as_bf16x8(dequant8(q1, s0)), acc);
-                acc = mfma16x16x32(as_bf16x8(a[4 * c + 2]), as_bf16x8(dequant8(q2, s1)), acc);
-                acc = mfma16x16x32(as_bf16x8(a[4 * c + 3]), as_bf16x8(dequant8(q3, s1)), acc);
+                acc = mfma16x16x32(as_bf16x8(a[4 * c]), as_bf16x8(dequant8_stream(q0, s0)), acc);
+                acc = mfma16x16x32(as_bf16x8(a[4 * c + 1]), as_bf16x8(dequant8_stream(q1, s0)), acc);
+                acc = mfma16x16x32(as_bf16x8(a[4 * c + 2]), as_bf16x8(dequant8_stream(q2, s1)), acc);
+                acc = mfma16x16x32(as_bf16x8(a[4 * c + 3]), as_bf16x8(dequant8_stream(q3, s1)), acc);
             } else {  // INT4: exact integer codes within the group, then its scale
                 const u32x4 q = v[c];
                 const uint32_t q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
@@ -336,12 +338,16 @@ __global__ __launch_bounds__(512) void decode_few_kernel(FArgs a)
     // memory operations complete in order, so a write-through store ahead of a weight load
     // would hold up the wait for that load by the store's round trip, every block.
     {
+        // Workgroup b takes blocks b, b + 256, b + 512, ...: the units' blocks are dealt out in
+        // unit order, so most units' h is complete long before the down phase needs it
+        // (contiguous ranges had every unit finish with its workgroups' last blocks).
         const int bpu = I / 8, nbk = nunits * bpu;
-        const int b0 = (int)((int64_t)nbk * b / kFG), b1 = (int)((int64_t)nbk * (b + 1) / kFG);
+        const int b0 = 0, b1 = nbk > b ? (nbk - b + kFG - 1) / kFG : 0;  // this workgroup's blocks, counted
         const size_t srow = scale_row_bytes(FMT, H);
         u32x4 wv[GD][NCG];
         uint32_t ws[GD][NCG];
-        auto issue = [&](int blk, u32x4 *v, uint32_t *sc) {
+        auto issue = [&](int jb, u32x4 *v, uint32_t *sc) {  // this workgroup's block jb
+            const int blk = b + kFG * jb;
             const int u = blk / bpu, i = (blk - u * bpu) * 8 + (r & 7), e = sh.u_e[u];
             const WMat &m = r < 8 ? a.w.gate : a.w.up;
             if (FMT == 0) {
@@ -361,7 +367,8 @@ __global__ __launch_bounds__(512) void decode_few_kernel(FArgs a)
             }
         };
         // the last wave: lane = (token m, pairs q0 and q0 + 1 of the block)
-        auto epilogue = [&](int blk) {
+        auto epilogue = [&](int jb) {
+            const int blk = b + kFG * jb;
             const int u = blk / bpu, i0 = (blk - u * bpu) * 8;
             const int m = lane >> 2, q0 = 2 * (lane & 3);
             const int slot = m < T ? sh.u_tslot[u][m] : -1;

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
                 if (FMT == 1) {
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        const bf16x8 bv = as_bf16x8(dequant8(qv[q][j], e4m3_to_f32((sb[q] >> (8 * (j >> 1))) & 0xffu)));
+                        const bf16x8 bv = as_bf16x8(dequant8_stream(qv[q][j], e4m3_to_f32((sb[q] >> (8 * (j >> 1))) & 0xffu)));
                         acc[q] = mfma16x16x32(as_bf16x8(a[j]), bv, acc[q]);
                     }
                 } else {
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                     if (FMT == 1) {
 #pragma unroll
                         for (int j = 0; j < 4; j++) {
-                            const bf16x8 bv = as_bf16x8(dequant8(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
+                            const bf16x8 bv = as_bf16x8(dequant8_stream(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
                             acc = mfma16x16x32(as_bf16x8(a[i][j]), bv, acc);
                         }
                     } else {  // INT4: integer codes per scale group, then the row's group scale
