@@ -436,7 +436,7 @@ def run_config(name, args, torch, fm, dg, pools):
                   "decode1_kernel (one persistent launch per layer; chain time / layers)" if chain and T == 1 else
                   "decode_few_kernel (one persistent launch per layer; chain time / layers)" if chain else
                   "decode1_kernel (the whole layer in one persistent launch)" if T == 1 else
-                  "decode_few_kernel (the whole layer in one persistent launch)" if T <= 16 else
+                  "decode_few_kernel (the whole layer in one persistent launch)" if T <= 16 and fmt == 0 else
                   "one layer call: router with selection, gate/up, down and combine kernels")
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
