@@ -3,7 +3,8 @@
 // Prefill is compute-heavy rather than weight-bound (recipes.vllm.ai "RecursiveSI/flint",
 // Benchmarking: the NVFP4 checkpoint barely changes the 8K-token prefill time), so the
 // expert FFNs run on bf16 MFMA with fp32 accumulation and LDS-staged tiles: bf16 weights
-// through a ring of K stages filled HBM -> LDS directly (gemm_bf16_kernel); 4-bit weights as
+// through a ring of K stages filled HBM -> LDS directly (gemm_bf16k64_kernel, 64-wide
+// stages; gemm_bf16_kernel, 32-wide, for a down pass with I % 64 == 32); 4-bit weights as
 // their codes through a register ring, dequantised once into a bf16 LDS stage
 // (gemm_q4_kernel, K a multiple of 128); NVFP4 weights whose K is not a multiple of 128
 // through registers into a padded double buffer, dequantised on the way, with a prefetch of
@@ -190,9 +191,11 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
 // 256 B rows of 64 bytes), filled HBM -> LDS by global_load_lds_dwordx4 (no registers)
 // NS - 1 stages ahead, so three or four stages of loads are in flight per CU while the
 // MFMAs consume the oldest one, and each stage costs one barrier.  Row R keeps its
-// 16-byte chunk c at slot c ^ ((R >> 2) & 3): the 16 lanes of one MFMA fragment read
-// (rows r, chunk g) and one copy instruction writes 16 whole rows, both without bank
-// conflicts (padding the rows instead left conflicts on both sides).
+// 16-byte chunk c at slot c ^ ((R >> 1) & 3).  A fragment read (lane (g, r): row r of a
+// 16-row group, chunk g) then runs at the LDS's full 256 bytes per clock; measured on
+// gfx950, the same read with c ^ ((R >> 2) & 3) or unswizzled 64-byte rows takes twice as
+// long (two-way bank conflicts).  A copy instruction writes 1 KB of LDS contiguously (16
+// whole rows), so the swizzle only decides which global chunk each lane fetches.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -229,9 +232,9 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
     const int wm = wave >> 2, wn = wave & 3;
 
     // Copies: wave w fills A rows and B rows 16 w .. 16 w + 15 of every stage; lane l takes
-    // row 16 w + l / 4, slot l % 4, i.e. logical chunk (l % 4) ^ ((row >> 2) & 3).
+    // row 16 w + l / 4, slot l % 4, i.e. logical chunk (l % 4) ^ ((row >> 1) & 3).
     const int crow = 16 * wave + (lane >> 2);
-    const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);
+    const int cchunk = (lane & 3) ^ ((crow >> 1) & 3);
     const uint16_t *ap_;
     const uint16_t *bp_;
     {
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Fragment reads: A row wm*64 + 16 ms + r and B row wn*64 + 16 ns + r, logical chunk g.
-    const int fslot = 16 * (g ^ ((r >> 2) & 3));
+    const int fslot = 16 * (g ^ ((r >> 1) & 3));
     const int aoff = (wm * 64 + r) * kRow + fslot, boff = kTile + (wn * 64 + r) * kRow + fslot;
     const int nk = K / 32;  // >= 4
 #pragma unroll
@@ -301,6 +304,136 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
         for (int ms = 0; ms < 4; ms++)
 #pragma unroll
             for (int ns = 0; ns < 4; ns++) acc[ms][ns] = mfma16x16x32(af[ms], bfr[ns], acc[ms][ns]);
+    }
+
+    // Epilogue.  acc[ms][ns][i] = D[row = wm*64 + ms*16 + 4g + i][brow = wn*64 + ns*16 + r].
+#pragma unroll
+    for (int ms = 0; ms < 4; ms++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = wm * 64 + ms * 16 + 4 * g + i;
+            if (row >= valid) continue;
+            const size_t slot = (size_t)(base + m0 + row);
+            if (MODE == 0) {
+#pragma unroll
+                for (int ns = 0; ns < 2; ns++) {
+                    const int col = nb * (BN / 2) + wn * 32 + ns * 16 + r;
+                    if (col < I) out[slot * I + col] = (uint16_t)f2bf(silu(acc[ms][ns][i]) * acc[ms][ns + 2][i]);
+                }
+            } else {
+#pragma unroll
+                for (int ns = 0; ns < 4; ns++) {
+                    const int col = nb * BN + wn * 64 + ns * 16 + r;
+                    if (col < H) out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bf16: 64-wide K stages
+// The 16-wave kernel with K stages of 64 (128-byte row pieces, whole cache lines): a copy
+// instruction fetches 8 rows x 128 B, so the same bytes take half as many L2 requests as
+// with 64-byte pieces, whose kernel spent 61 % of its cycles with the CU's L1 stalled on
+// pending requests (counters); this one measured 5 % faster.  Two stages of 64 KB: the
+// copies of stage kt + 1 fly while stage kt is multiplied.
+// Row R keeps its 16-byte chunk c at slot c ^ (R & 7), conflict-free for the fragment reads
+// (lane (g, r): row r, chunk 4 j + g in K half j).  K must be a multiple of 64.
+template <int MODE>
+__global__ __launch_bounds__(NT) void gemm_bf16k64_kernel(int T, int H, int I, int E, int k, WSet w,
+                                                          const uint16_t *__restrict__ asrc,
+                                                          const int32_t *__restrict__ sa, Plan p,
+                                                          uint16_t *__restrict__ out)
+{
+    constexpr int kRow = 128, kTile = 256 * kRow, kStage = 2 * kTile;  // bytes
+    extern __shared__ __attribute__((aligned(16))) uint8_t ring[];      // 2 * kStage
+    const int N = MODE == 0 ? 2 * I : H;
+    const int n_tiles = (N + BN - 1) / BN;
+    int item, nb;
+    xcd_map(blockIdx.x, n_tiles, item, nb);
+    if (item >= p.meta[1]) return;
+    const int code = p.items[item];
+    const int u = code >> 16, mtile = code & 0xffff;
+    const int e = p.touched[u], base = p.tbase[u], cnt = p.tcount[u];
+    const bool sh = (e == E);
+    const int m0 = mtile * BM;
+    const int valid = min(BM, cnt - m0);
+    const int K = MODE == 0 ? H : I;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int wm = wave >> 2, wn = wave & 3;
+
+    // Copies: wave w fills A rows and B rows 16 w + 8 c + l / 8 (c < 2) of every stage,
+    // slot l % 8, i.e. logical chunk (l % 8) ^ (row & 7).
+    const uint16_t *ap_[2];
+    const uint16_t *bp_[2];
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+        const int crow = 16 * wave + 8 * c + (lane >> 3);
+        const int cchunk = (lane & 7) ^ (crow & 7);
+        const int ri = min(crow, valid - 1);
+        if (MODE == 0) {
+            const int tok = sh ? base - T * k + m0 + ri : sa[base + m0 + ri] / k;
+            ap_[c] = asrc + (size_t)tok * H + 8 * cchunk;
+        } else {
+            ap_[c] = asrc + (size_t)(base + m0 + ri) * I + 8 * cchunk;
+        }
+        const WMat *mat;
+        int n;
+        if (MODE == 0) {  // each 64-row wave column: 32 gate rows, then the same 32 up rows
+            const int wcol = crow >> 6, within = crow & 63;
+            mat = (within >> 5) ? &w.up : &w.gate;
+            n = min(nb * (BN / 2) + wcol * 32 + (within & 31), I - 1);
+        } else {
+            mat = &w.down;
+            n = min(nb * BN + crow, H - 1);
+        }
+        const size_t mb = (size_t)H * I;
+        bp_[c] = reinterpret_cast<const uint16_t *>(sh ? mat->shared : mat->routed) + (sh ? 0 : (size_t)e * mb) +
+                 (size_t)n * K + 8 * cchunk;
+    }
+    uint8_t *const cdst = ring + 2048 * wave;  // + stage * kStage (+ kTile for B)
+    auto issue = [&](int kt) {
+        uint8_t *st = cdst + (size_t)(kt & 1) * kStage;
+        lds_copy16(ap_[0] + 64 * kt, st);
+        lds_copy16(ap_[1] + 64 * kt, st + 1024);
+        lds_copy16(bp_[0] + 64 * kt, st + kTile);
+        lds_copy16(bp_[1] + 64 * kt, st + kTile + 1024);
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment reads: A row wm*64 + 16 ms + r and B row wn*64 + 16 ns + r, logical chunk
+    // 4 j + g for the K half j of the stage.
+    const int aoff = (wm * 64 + r) * kRow, boff = kTile + (wn * 64 + r) * kRow;
+    const int fs0 = 16 * (g ^ (r & 7)), fs1 = 16 * ((4 + g) ^ (r & 7));
+    const int nk = K / 64;
+    issue(0);
+    for (int kt = 0; kt < nk; kt++) {
+        // stage kt is the only one in flight: once it has landed for every wave, the slot
+        // read in iteration kt - 1 is free for stage kt + 1
+        wait_vmcnt<0>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + 1 < nk) issue(kt + 1);
+        const uint8_t *st = ring + (size_t)(kt & 1) * kStage;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int fs = j ? fs1 : fs0;
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int ms = 0; ms < 4; ms++) af[ms] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + aoff + ms * 16 * kRow + fs));
+#pragma unroll
+            for (int ns = 0; ns < 4; ns++) bfr[ns] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + boff + ns * 16 * kRow + fs));
+#pragma unroll
+            for (int ms = 0; ms < 4; ms++)
+#pragma unroll
+                for (int ns = 0; ns < 4; ns++) acc[ms][ns] = mfma16x16x32(af[ms], bfr[ns], acc[ms][ns]);
+        }
     }
 
     // Epilogue.  acc[ms][ns][i] = D[row = wm*64 + ms*16 + 4g + i][brow = wn*64 + ns*16 + r].
@@ -370,12 +503,12 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
     const int wm = wave >> 1, wn = wave & 1;
 
     // A copies: wave w fills rows 32 w + 16 c + l / 4 (c < 2) of every stage, slot l % 4,
-    // i.e. logical chunk (l % 4) ^ ((row >> 2) & 3).  Rows past the tile repeat the last.
+    // i.e. logical chunk (l % 4) ^ ((row >> 1) & 3).  Rows past the tile repeat the last.
     const uint16_t *ap_[2];
 #pragma unroll
     for (int c = 0; c < 2; c++) {
         const int crow = 32 * wave + 16 * c + (lane >> 2);
-        const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);
+        const int cchunk = (lane & 3) ^ ((crow >> 1) & 3);
         const int ri = min(crow, valid - 1);
         if (MODE == 0) {
             const int tok = sh ? base - T * k + m0 + ri : sa[base + m0 + ri] / k;
@@ -421,7 +554,7 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
     auto dequant_b = [&](int kt, int slot) {  // stage kt's codes -> bf16 B buffer kt % 2
         const float sc = FMT == 1 ? e4m3_to_f32(cs[slot]) : bf2f(cs[slot]);
         uint8_t *row = bbuf + (kt & 1) * kStage + bro * kRow;
-        const int sw = (bro >> 2) & 3;
+        const int sw = (bro >> 1) & 3;
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++) {
             const uint32_t qw = cq[slot][h2];
@@ -437,7 +570,7 @@ __global__ __launch_bounds__(NTQ) void gemm_q4_kernel(int T, int H, int I, int E
         for (int j = 0; j < 8; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Fragment reads: A row wm*64 + 16 ms + r and B row wn*128 + 16 ns + r, logical chunk g.
-    const int fslot = 16 * (g ^ ((r >> 2) & 3));
+    const int fslot = 16 * (g ^ ((r >> 1) & 3));
     const int aoff = (wm * 64 + r) * kRow + fslot, boff = (wn * 128 + r) * kRow + fslot;
     auto compute = [&](int kt) {
         const uint8_t *as = lds + (kt % NSA) * kStage + aoff;
@@ -581,9 +714,14 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
     const unsigned g1 = (unsigned)(item_slots * ((2 * s.I + BN - 1) / BN));
     const unsigned g2 = (unsigned)(item_slots * ((s.H + BN - 1) / BN));
     if (w.fmt == 0) {
-        constexpr size_t lds = (size_t)kRingStages * 2 * 256 * 64;
-        gemm_bf16_kernel<0, kRingStages><<<g1, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
-        gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        // 64-wide K stages (H is a multiple of 64); the down pass with I % 64 == 32 takes the
+        // 32-wide ring
+        constexpr size_t lds32 = (size_t)kRingStages * 2 * 256 * 64, lds64 = (size_t)2 * 2 * 256 * 128;
+        gemm_bf16k64_kernel<0><<<g1, NT, lds64, st>>>((int)T, s.H, s.I, s.E, s.k, w, x, sa, plan, h);
+        if (s.I % 64 == 0)
+            gemm_bf16k64_kernel<1><<<g2, NT, lds64, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+        else
+            gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds32, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
     } else {
         // 4-bit weights: the code ring needs K in whole trips of four 32-wide stages (INT4
         // always has them: its scale groups are 128 columns); NVFP4 with K % 128 != 0 takes
