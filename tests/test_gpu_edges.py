@@ -341,14 +341,15 @@ def test_forced_timeout_is_reported_and_cleared(kind):
 
 # ---------------------------------------------------------------- shapes past the 256/128 grid
 @pytest.mark.parametrize("fmt", [fm.WFMT_BF16, fm.WFMT_NVFP4])
-@pytest.mark.parametrize("H,I", [(320, 96), (192, 160)])
+@pytest.mark.parametrize("H,I", [(320, 96), (192, 160), (64, 64)])
 @pytest.mark.parametrize("T", [1, 8, 33, 300])
 def test_shapes_h64_i32(T, H, I, fmt):
     """H a multiple of 64 but not of 128 or 256, I a multiple of 32 but not of 128: K tails
     in the streaming kernels, partial N tiles in the grouped GEMMs and, for NVFP4, the
     register-staged GEMM with zeros past K; T = 1 takes the small-batch router launch (the
     single-token launch needs H % 256 == 0) and T = 8 with bf16 weights the one-launch
-    small-batch layer."""
+    small-batch layer.  bf16 grouped GEMMs: I % 64 == 32 sends the down pass to the 32-wide
+    ring; H = I = 64 runs both passes on the 64-wide kernel with a single K stage."""
     _say("case T=%d H=%d I=%d fmt=%d" % (T, H, I, fmt))
     c = Case(T, H, I, 256, 6, fmt=fmt)
     g, ws = _run(c)
