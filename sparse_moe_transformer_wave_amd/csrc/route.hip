@@ -46,9 +46,16 @@ __global__ __launch_bounds__(256) void router_small_kernel(int T, int H, int E,
 // 32-K step and its 4 token fragments serve all of them (the weight parts are the larger
 // operand: splitting the tile by tokens only made every wave re-read all 3 x 64 expert
 // rows from LDS).  Global loads run two K steps ahead in registers (stage k + 2 is
-// fetched while stage k is multiplied and stage k + 1 waits to be split into LDS).
+// fetched while stage k is multiplied and stage k + 1 waits to be split into LDS).  LDS
+// rows are 128 bytes with 16-byte chunk c of row R at slot c ^ (R & 7): the fragment reads
+// (16 rows, one chunk each) then run at the LDS's full rate; with rows padded to 144 bytes
+// they took twice as long (two-way bank conflicts, measured on gfx950).  The kernel's time
+// barely moved with it (54.8 -> 53.8 us at T = 8192): its reads are not what bounds it.
 namespace {
-constexpr int RBM = 128, RBN = 64, RBK = 64, RLD = RBK + 8;
+constexpr int RBM = 128, RBN = 64, RBK = 64;
+
+// byte offset of 16-byte chunk c (of 8) of row R in a 128-byte-row tile
+__device__ __forceinline__ int rsw(int R, int c) { return R * 128 + 16 * (c ^ (R & 7)); }
 
 __device__ __forceinline__ uint32_t trunc_bf16(float v) { return __float_as_uint(v) >> 16; }
 
@@ -65,8 +72,8 @@ __global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
                                                           const float *__restrict__ bias,
                                                           float *__restrict__ logits)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][RBM][RLD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][RBN][RLD];
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][RBM * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][3][RBN * 128];
     const int t0 = blockIdx.x * RBM, e0 = blockIdx.y * RBN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int we = wave & 3, wt = wave >> 2;  // expert group, token half
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int c = tid + RNT * j;
-            *reinterpret_cast<u32x4 *>(&As[buf][c >> 3][(c & 7) * 8]) = st.a[j];
+            *reinterpret_cast<u32x4 *>(&As[buf][rsw(c >> 3, c & 7)]) = st.a[j];
             const float vv[4] = {st.b[j].x, st.b[j].y, st.b[j].z, st.b[j].w};
             uint32_t hi[4], mid[4], lo[4];
 #pragma unroll
@@ -103,10 +110,11 @@ __global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
                 const float r2 = r1 - __uint_as_float(mid[q] << 16);
                 lo[q] = f2bf(r2);
             }
-            const int row = c >> 4, col = (c & 15) * 4;
-            *reinterpret_cast<u32x2 *>(&Bs[buf][0][row][col]) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-            *reinterpret_cast<u32x2 *>(&Bs[buf][1][row][col]) = u32x2{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16)};
-            *reinterpret_cast<u32x2 *>(&Bs[buf][2][row][col]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+            const int row = c >> 4, q = c & 15;  // 8 bytes: half q % 2 of chunk q / 2
+            const int off = rsw(row, q >> 1) + 8 * (q & 1);
+            *reinterpret_cast<u32x2 *>(&Bs[buf][0][off]) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+            *reinterpret_cast<u32x2 *>(&Bs[buf][1][off]) = u32x2{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16)};
+            *reinterpret_cast<u32x2 *>(&Bs[buf][2][off]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
         }
     };
     auto compute = [&](int buf) {
@@ -115,10 +123,10 @@ __global__ __launch_bounds__(RNT) void router_mfma_kernel(int T, int H, int E,
             bf16x8 bfr[3];
 #pragma unroll
             for (int part = 0; part < 3; part++)
-                bfr[part] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bs[buf][part][we * 16 + r][kk * 32 + g * 8]));
+                bfr[part] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Bs[buf][part][rsw(we * 16 + r, kk * 4 + g)]));
 #pragma unroll
             for (int ms = 0; ms < 4; ms++) {
-                const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4 *>(&As[buf][wt * 64 + ms * 16 + r][kk * 32 + g * 8]));
+                const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4 *>(&As[buf][rsw(wt * 64 + ms * 16 + r, kk * 4 + g)]));
 #pragma unroll
                 for (int part = 0; part < 3; part++) acc[ms] = mfma16x16x32(af, bfr[part], acc[ms]);
             }
