@@ -4,7 +4,7 @@
 // Benchmarking: the NVFP4 checkpoint barely changes the 8K-token prefill time), so the
 // expert FFNs run on bf16 MFMA with fp32 accumulation and LDS-staged tiles: bf16 weights
 // through a ring of K stages filled HBM -> LDS directly (gemm_bf16k64_kernel, 64-wide
-// stages; gemm_bf16_kernel, 32-wide, for a down pass with I % 64 == 32); 4-bit weights as
+// stages; gemm_bf16_down_kernel, 32-wide, for a down pass with I % 64 == 32); 4-bit weights as
 // their codes through a register ring, dequantised once into a bf16 LDS stage
 // (gemm_q4_kernel, K a multiple of 128); NVFP4 weights whose K is not a multiple of 128
 // through registers into a padded double buffer, dequantised on the way, with a prefetch of
@@ -185,8 +185,10 @@ __global__ __launch_bounds__(NT) void grouped_gemm_kernel(int T, int H, int I, i
     }
 }
 
-// ---------------------------------------------------------------- bf16: LDS ring
-// The same tiles and work items for bf16 weights, with the K loop rebuilt around the
+// ---------------------------------------------------------------- bf16: 32-wide LDS ring
+// The down pass when I % 64 == 32 (K = I not a whole number of 64-wide stages; the
+// 64-wide kernel below takes every other bf16 pass).  The same tiles and work items as
+// the other grouped GEMMs, with the K loop built around the
 // CU's LDS: K runs in stages of 32 through a ring of NS stages (32 KB each: 256 A rows and
 // 256 B rows of 64 bytes), filled HBM -> LDS by global_load_lds_dwordx4 (no registers)
 // NS - 1 stages ahead, so three or four stages of loads are in flight per CU while the
@@ -208,16 +210,14 @@ __device__ __forceinline__ void lds_copy16(const void *g, uint8_t *lds)
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
-template <int MODE, int NS>
-__global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int E, int k, WSet w,
-                                                       const uint16_t *__restrict__ asrc,
-                                                       const int32_t *__restrict__ sa, Plan p,
-                                                       uint16_t *__restrict__ out)
+template <int NS>
+__global__ __launch_bounds__(NT) void gemm_bf16_down_kernel(int H, int I, int E, WSet w,
+                                                            const uint16_t *__restrict__ asrc, Plan p,
+                                                            uint16_t *__restrict__ out)
 {
     constexpr int kRow = 64, kTile = 256 * kRow, kStage = 2 * kTile;  // bytes
     extern __shared__ __attribute__((aligned(16))) uint8_t ring[];     // NS * kStage
-    const int N = MODE == 0 ? 2 * I : H;
-    const int n_tiles = (N + BN - 1) / BN;
+    const int n_tiles = (H + BN - 1) / BN;
     int item, nb;
     xcd_map(blockIdx.x, n_tiles, item, nb);
     if (item >= p.meta[1]) return;
@@ -227,11 +227,12 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
     const bool sh = (e == E);
     const int m0 = mtile * BM;
     const int valid = min(BM, cnt - m0);
-    const int K = MODE == 0 ? H : I;
+    const int K = I;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int wm = wave >> 2, wn = wave & 3;
 
-    // Copies: wave w fills A rows and B rows 16 w .. 16 w + 15 of every stage; lane l takes
+    // Copies: wave w fills A rows (h rows of the item's slots) and B rows (down rows)
+    // 16 w .. 16 w + 15 of every stage; lane l takes
     // row 16 w + l / 4, slot l % 4, i.e. logical chunk (l % 4) ^ ((row >> 1) & 3).
     const int crow = 16 * wave + (lane >> 2);
     const int cchunk = (lane & 3) ^ ((crow >> 1) & 3);
@@ -239,24 +240,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
     const uint16_t *bp_;
     {
         const int ri = min(crow, valid - 1);
-        if (MODE == 0) {
-            const int tok = sh ? base - T * k + m0 + ri : sa[base + m0 + ri] / k;
-            ap_ = asrc + (size_t)tok * H + 8 * cchunk;
-        } else {
-            ap_ = asrc + (size_t)(base + m0 + ri) * I + 8 * cchunk;
-        }
-        const WMat *mat;
-        int n;
-        if (MODE == 0) {  // each 64-row wave column: 32 gate rows, then the same 32 up rows
-            const int wcol = crow >> 6, within = crow & 63;
-            mat = (within >> 5) ? &w.up : &w.gate;
-            n = min(nb * (BN / 2) + wcol * 32 + (within & 31), I - 1);
-        } else {
-            mat = &w.down;
-            n = min(nb * BN + crow, H - 1);
-        }
+        ap_ = asrc + (size_t)(base + m0 + ri) * I + 8 * cchunk;
+        const int n = min(nb * BN + crow, H - 1);
         const size_t mb = (size_t)H * I;
-        bp_ = reinterpret_cast<const uint16_t *>(sh ? mat->shared : mat->routed) + (sh ? 0 : (size_t)e * mb) +
+        bp_ = reinterpret_cast<const uint16_t *>(sh ? w.down.shared : w.down.routed) + (sh ? 0 : (size_t)e * mb) +
               (size_t)n * K + 8 * cchunk;
     }
     uint8_t *const cdst = ring + 1024 * wave;  // + stage * kStage (+ kTile for B)
@@ -314,18 +301,10 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(int T, int H, int I, int 
             const int row = wm * 64 + ms * 16 + 4 * g + i;
             if (row >= valid) continue;
             const size_t slot = (size_t)(base + m0 + row);
-            if (MODE == 0) {
 #pragma unroll
-                for (int ns = 0; ns < 2; ns++) {
-                    const int col = nb * (BN / 2) + wn * 32 + ns * 16 + r;
-                    if (col < I) out[slot * I + col] = (uint16_t)f2bf(silu(acc[ms][ns][i]) * acc[ms][ns + 2][i]);
-                }
-            } else {
-#pragma unroll
-                for (int ns = 0; ns < 4; ns++) {
-                    const int col = nb * BN + wn * 64 + ns * 16 + r;
-                    if (col < H) out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i]);
-                }
+            for (int ns = 0; ns < 4; ns++) {
+                const int col = nb * BN + wn * 64 + ns * 16 + r;
+                if (col < H) out[slot * H + col] = (uint16_t)f2bf(acc[ms][ns][i]);
             }
         }
     }
@@ -462,7 +441,7 @@ __global__ __launch_bounds__(NT) void gemm_bf16k64_kernel(int T, int H, int I, i
 }
 
 // ---------------------------------------------------------------- NVFP4 / INT4: codes to LDS once
-// The same 256 x 256 tiles as gemm_bf16_kernel, here with 8 waves (two per SIMD) of
+// The same 256 x 256 tiles as the bf16 kernels, here with 8 waves (two per SIMD) of
 // 64 slots x 128 B rows each, so the registers hold what the 4-bit path adds.  The tokens
 // (A) come through a 5-stage ring of 32-wide K stages filled HBM -> LDS by
 // global_load_lds_dwordx4, four stages ahead.  The weights arrive as their 4-bit codes:
@@ -721,7 +700,7 @@ hipError_t launch_gemm_forward(const Shape &s, const WSet &w, int64_t T, const u
         if (s.I % 64 == 0)
             gemm_bf16k64_kernel<1><<<g2, NT, lds64, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
         else
-            gemm_bf16_kernel<1, kRingStages><<<g2, NT, lds32, st>>>((int)T, s.H, s.I, s.E, s.k, w, h, sa, plan, o);
+            gemm_bf16_down_kernel<kRingStages><<<g2, NT, lds32, st>>>(s.H, s.I, s.E, w, h, plan, o);
     } else {
         // 4-bit weights: the code ring needs K in whole trips of four 32-wide stages (INT4
         // always has them: its scale groups are 128 columns); NVFP4 with K % 128 != 0 takes
