@@ -38,15 +38,15 @@
  *     FLINT_ERR_SHAPE.
  *   - Calls on one stream are ordered; calls that share a workspace must not overlap.
  *   - A workspace's first 4 MiB (the head) hold the persistent launches' launch counters,
- *     the error flags, the small-batch arrival counter and exchange words: zero them once
- *     before first use (flint_moe_workspace_init, or any zero fill) and leave them to the
- *     library afterwards.  Head words: u32 at byte 8 = error flags (read and cleared by
- *     flint_moe_workspace_status); u32 at byte 12 = the small-batch arrival counter; u32 at
- *     byte 16 = a diagnostic switch, 0 in normal use: nonzero makes every bounded wait of
- *     the persistent launches give up at once (it exists so that the timeout report can be
- *     tested; results are then unreliable); u32 [256] at byte 1024 = launch counters, each
- *     the number of persistent launches (single-token and small-batch layer launches) made
- *     on the workspace so far.
+ *     the error flags and exchange words: zero them once before first use
+ *     (flint_moe_workspace_init, or any zero fill) and leave them to the library
+ *     afterwards.  Head words: u32 at byte 8 = error flags (read and cleared by
+ *     flint_moe_workspace_status); u32 at byte 12 = reserved; u32 at byte 16 = a diagnostic
+ *     switch, 0 in normal use: nonzero makes every bounded wait of the persistent launches
+ *     give up at once (it exists so that the timeout report can be tested; results are then
+ *     unreliable); u32 [256] at byte 1024 = launch counters, each the number of persistent
+ *     launches (single-token and small-batch layer launches, small-batch router launches)
+ *     made on the workspace so far.
  */
 #ifndef FLINT_MOE_H
 #define FLINT_MOE_H
@@ -72,7 +72,8 @@ enum {
 /* ---- workspace error flags (flint_moe_workspace_status) ---------------------------- */
 enum {
     /* A bounded wait of a persistent launch (the single-token layer, the dense single-token
-       layer, every layer of a decode chain) ran out: its workgroups were not all resident
+       layer, the small-batch layer and its router launch, every layer of a decode chain)
+       ran out: its workgroups were not all resident
        at once (another kernel held CUs), so that call's outputs are unreliable.  The
        launch still ended normally, and later calls are unaffected: every launch's exchange
        words carry a tag of their own. */
@@ -226,7 +227,11 @@ int flint_moe_forward(const flint_moe_desc *desc, const flint_moe_weights *weigh
    exchange logits and h through tagged words at the start of the workspace (see
    flint_moe_workspace_init); it rounds h to bf16 like the other paths and combines the
    per-slot outputs in fp32; a dense layer's single bf16 token likewise (see
-   flint_moe_forward).  These launches need all 256 workgroups resident at once; they are
+   flint_moe_forward).  2 <= T <= 16 tokens with bf16 weights run as one persistent launch
+   of the whole layer in the same way; other batches of up to 32 tokens compute the logits,
+   the top-k selection, the grouping and the expert plan in one persistent launch (logits
+   exchanged as tagged words) before the expert kernels, with the results of the route and
+   permute calls.  These launches need all 256 workgroups resident at once; they are
    chosen only on a device with at least 256 CUs where one workgroup fits on a CU.  A wait
    there that runs out (other work holding CUs) raises FLINT_WS_WAIT_TIMEOUT in the
    workspace (flint_moe_workspace_status). */

@@ -30,7 +30,7 @@ ROUTE_LOGITS_IN = 1
 CHAIN_RESIDUAL = 1
 WS_WAIT_TIMEOUT = 1
 # byte offsets of the workspace head's words (include/flint_moe.h)
-HEAD_ERROR, HEAD_ARRIVALS, HEAD_DIAG, HEAD_COUNTERS = 8, 12, 16, 1024
+HEAD_ERROR, HEAD_DIAG, HEAD_COUNTERS = 8, 16, 1024
 
 EXPORTED = ("flint_moe_workspace_bytes", "flint_moe_workspace_init", "flint_moe_workspace_status",
             "flint_moe_status_string",

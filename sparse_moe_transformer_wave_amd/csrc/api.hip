@@ -433,9 +433,9 @@ int flint_moe_layer(const flint_moe_desc *desc, const flint_moe_weights *weights
         return hip_status(launch_decode_few(s, wset_of(weights), T, x, w_router, logit_bias, y, lg, ids, tw,
                                             cnt, off, sa, ap, b + L.sync, st));
     }
-    if (T <= kGemvMaxT) {
+    if (router_select_supported(s, T)) {  // T <= kGemvMaxT: one persistent launch
         rc = hip_status(launch_router_select(s, T, x, w_router, logit_bias, lg, ids, tw, cnt, off,
-                                             sa, ap, plan, (int *)(b + L.sync + kHeadArrivals), st));
+                                             sa, ap, plan, (uint8_t *)(b + L.sync), st));
         if (rc) return rc;
     } else {
         rc = hip_status(launch_router(s, T, x, w_router, logit_bias, lg, st));

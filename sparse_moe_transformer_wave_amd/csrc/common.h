@@ -89,25 +89,27 @@ hipError_t launch_permute(const Shape &s, int64_t T, const int32_t *ids, int32_t
                           int32_t *hist, hipStream_t st);
 hipError_t launch_plan(const Shape &s, int64_t T, const int32_t *offsets, const Plan &plan,
                        hipStream_t st);
-// 2 <= T <= kGemvMaxT: router, then (in the last workgroup to finish) top-k, grouping and
-// plan, in one launch.  `arrivals` = a zero-initialised word of the workspace head; every
-// launch leaves it zero.
+// T <= kGemvMaxT: router, top-k, grouping and plan in one persistent launch (kPersistentGrid
+// workgroups of 1024 threads exchanging logits through tagged words in the workspace head);
+// supported when every workgroup fits at once, E <= 256, k <= 8 and S <= 1.
+bool router_select_supported(const Shape &s, int64_t T);
 hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, const float *Wr,
                                 const float *bias, float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap,
-                                const Plan &plan, int *arrivals, hipStream_t st);
+                                const Plan &plan, uint8_t *head, hipStream_t st);
 // Workspace head: the first kSyncBytes of every workspace (zeroed once before first use).
 //   u32 at kHeadError     error flags (FLINT_WS_WAIT_TIMEOUT); cleared by the status call
-//   u32 at kHeadArrivals  arrival counter of the small-batch router launch (re-armed by it)
+//   u32 at kHeadReserved  unused (zero)
 //   u32 at kHeadDiag      diagnostic switch: nonzero makes every bounded wait give up at once
 //   u32 [kPersistentGrid] at kHeadCounters  launch counters, one per workgroup index: every
 //                         persistent launch has exactly kPersistentGrid workgroups and
 //                         workgroup b adds one to counter b, so all counters hold the number
 //                         of persistent launches before the current one, which gives its tag
 //   exchange words of the persistent launches from kHeadXchg on: the single-token layers'
-//   up to kHeadFewXchg, the small-batch layer's from there (4 MiB in all)
+//   up to kHeadFewXchg, the small-batch layer's and the small-batch router launch's from
+//   there (4 MiB in all)
 constexpr size_t kSyncBytes = 4096 * 1024, kHeadFewXchg = 96 * 1024;
-constexpr size_t kHeadError = 8, kHeadArrivals = 12, kHeadDiag = 16, kHeadCounters = 1024, kHeadXchg = 2048;
+constexpr size_t kHeadError = 8, kHeadReserved = 12, kHeadDiag = 16, kHeadCounters = 1024, kHeadXchg = 2048;
 constexpr int kPersistentGrid = 256;
 constexpr uint32_t kWsWaitTimeout = 1u;  // FLINT_WS_WAIT_TIMEOUT
 static_assert(kHeadCounters + 4 * kPersistentGrid <= kHeadXchg, "launch counters overlap the exchange words");

@@ -7,6 +7,7 @@
 // An assignment whose id lies outside [0, E) is dropped: it is in no count, its
 // assign_pos is -1, and sorted_assign holds -1 past offsets[E] (every path below).
 #include "common.h"
+#include "xchg.h"
 
 namespace flint {
 
@@ -241,74 +242,119 @@ __device__ void group_plan_small(int T, int E, int k, int S, const int32_t *s_id
     }
 }
 
-// Small batches (T <= 32, unless the single-token launch takes T = 1): router and routing in
-// one launch.  Workgroup e (16 waves, wave w takes tokens w and w + 16) computes the logits
-// of expert e and writes them with agent-scope write-through stores; once they have
-// completed it counts itself in at an agent-scope arrival counter.  The workgroup that
-// arrives last has every logit: it reads them back with agent-scope loads into LDS, selects
-// the top-k of every token (one token per wave; four per wave measured slower at 32
-// tokens), groups the assignments by expert and writes the plan, so the expert kernels that
-// follow need no routing step of their own.  It also re-arms the counter.
+// Small batches (T <= 32, unless the single-token launch takes T = 1): router, selection,
+// grouping and plan in one persistent launch of kPersistentGrid workgroups (one per CU), so
+// the expert kernels that follow need no routing step of their own.  Workgroup e < E
+// (16 waves, wave w takes tokens w and w + 16) computes the logits of expert e and publishes
+// each as a tagged exchange word (xchg.h: the launch tag and the fp32 value in one 64-bit
+// agent-scope store).  Workgroups 0 and, for more than 16 tokens, 1 then select: wave w of
+// workgroup b polls the E words of token 16 b + w and picks its top-k (`topk_wave`).
+// Workgroup 1 publishes its tokens' selections as words too; workgroup 0 waits for them,
+// groups the assignments by expert and writes the plan.  Every other workgroup ends after
+// publishing its logits.
 //
-// The hand-off uses relaxed atomics, not release/acquire, and rests on how gfx950 carries
-// out agent-scope atomics: an agent-scope store is written through to the memory side,
-// which every XCD sees (global_store ... sc1), s_waitcnt vmcnt(0) returns only once the
-// memory side has acknowledged it, and an agent-scope load (sc1) reads the memory side, not
-// a stale L2 line.  So every logit store has reached the memory side before its
-// workgroup's counter increment is issued, and the last workgroup's loads are issued after
-// that increment returned.  A release/acquire pair at agent scope would add an L2
-// write-back and invalidate in every workgroup (buffer_wbl2 / buffer_inv sc1), which
-// measured far slower than this launch's whole selection.
+// An arrival counter instead of tagged words (each workgroup storing its logits, waiting
+// for the stores and incrementing one agent-scope counter, the last to arrive selecting for
+// every token) measured 11.9 / 18.7 µs per launch at T = 8 / 32 against 8.7 / 12.2 µs here:
+// the store wait, the 256 serialised increments, and 32 tokens on one CU's 4 SIMDs.
+// Every wait is bounded (kSpin tries); one that runs out sets the workspace head's error
+// flag, as in the other persistent launches.
 __global__ __launch_bounds__(1024) void router_select_kernel(
     int T, int H, int E, int k, int S, int renorm, const uint16_t *__restrict__ x,
     const float *__restrict__ Wr, const float *__restrict__ bias, float *__restrict__ logits,
     int32_t *__restrict__ ids, float *__restrict__ wout, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sa, int32_t *__restrict__ ap, Plan plan,
-    int *arrivals)
+    uint8_t *head)
 {
+    static_assert(kGemvMaxT <= 32, "two selecting workgroups of 16 waves");
     __shared__ SmallGroup g;
-    __shared__ float s_lg[kGemvMaxT * 256];
+    __shared__ float s_lg[16][256];  // the logits of this wave's token
     __shared__ int32_t s_ids[kGemvMaxT * 8];
     __shared__ float s_w[kGemvMaxT * 8];
-    __shared__ int s_last;
-    const int e = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-    float sums[2];
-    router_dot_wave<2>(T, H, e, wv, 16, x, Wr, sums);
-    const float bv = bias ? bias[e] : 0.f;
-    if (lane == 0)
+    __shared__ uint32_t s_tag, s_giveup;
+    const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    uint32_t launches = 0;
+    if (tid == 0) {
+        launches = read_launches(head);
+        s_tag = launch_tag(launches);
+        s_giveup = diag_word(head);
+    }
+    float sums[2] = {0.f, 0.f};
+    if (b < E) router_dot_wave<2>(T, H, b, wv, 16, x, Wr, sums);
+    __syncthreads();
+    const uint32_t tag = s_tag;
+    const bool giveup = s_giveup != 0;
+    // logit words [T][E], then the second selecting workgroup's {id, weight} word pairs
+    uint64_t *xl = reinterpret_cast<uint64_t *>(head + kHeadFewXchg);
+    uint64_t *xs = xl + (size_t)T * E;
+    if (b < E && lane == 0) {
+        const float bv = bias ? bias[b] : 0.f;
 #pragma unroll
         for (int q = 0; q < 2; q++) {
             const int t = wv + 16 * q;
-            if (t < T)
-                __hip_atomic_store(logits + (size_t)t * E + e, sums[q] + bv, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (t < T) {
+                const float l = sums[q] + bv;
+                logits[(size_t)t * E + b] = l;
+                put_word(xl + (size_t)t * E + b, tag, l);
+            }
         }
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's logit stores have completed
+    }
+    if (b >= (T + 15) / 16) {
+        if (tid == 0) bump_launches(head, launches);
+        return;
+    }
+    const int t = 16 * b + wv;  // this wave's token
+    if (t < T) {
+        uint64_t lw[4];
+        const int nq = (E - lane + 63) / 64;  // words of experts lane, lane + 64, ... below E
+#pragma unroll
+        for (int i = 0; i < 4; i++) lw[i] = i < nq ? get_word(xl + (size_t)t * E + lane + 64 * i) : 0ull;
+        await_words<4>(xl + (size_t)t * E + lane, 64, nq, lw, tag, head, giveup);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (i < nq) s_lg[wv][lane + 64 * i] = __uint_as_float((uint32_t)lw[i]);
+    }
     __syncthreads();
-    if (tid == 0)
-        s_last = __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (!s_last) return;
-    for (int i = tid; i < T * E; i += 1024)
-        s_lg[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) __hip_atomic_store(arrivals, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    for (int t = wv; t < T; t += 16) topk_wave(s_lg + (size_t)t * E, E, k, renorm, s_ids + t * k, s_w + t * k);
+    if (t < T) {
+        topk_wave(s_lg[wv], E, k, renorm, s_ids + t * k, s_w + t * k);
+        if (b > 0 && lane < k) {
+            const int a = (t - 16) * k + lane;
+            put_word(xs + 2 * a, tag, __int_as_float(s_ids[t * k + lane]));
+            put_word(xs + 2 * a + 1, tag, s_w[t * k + lane]);
+        }
+    }
+    if (b > 0) {
+        if (tid == 0) bump_launches(head, launches);
+        return;
+    }
+    if (T > 16 && tid < (T - 16) * k) {  // assignment 16 k + tid, selected by workgroup 1
+        uint64_t sw[2] = {get_word(xs + 2 * tid), get_word(xs + 2 * tid + 1)};
+        await_words<2>(xs + 2 * tid, 1, 2, sw, tag, head, giveup);
+        s_ids[16 * k + tid] = (int32_t)(uint32_t)sw[0];
+        s_w[16 * k + tid] = __uint_as_float((uint32_t)sw[1]);
+    }
     __syncthreads();
     for (int a = tid; a < T * k; a += 1024) {
         ids[a] = s_ids[a];
         wout[a] = s_w[a];
     }
     group_plan_small(T, E, k, S, s_ids, g, counts, offsets, sa, ap, plan);
+    if (tid == 0) bump_launches(head, launches);
+}
+
+bool router_select_supported(const Shape &s, int64_t T)
+{
+    return T >= 1 && T <= kGemvMaxT && s.E >= 1 && s.E <= 256 && s.k >= 1 && s.k <= 8 && s.S <= 1 &&
+           persistent_fits(reinterpret_cast<const void *>(&router_select_kernel), 1024, 0);
 }
 
 hipError_t launch_router_select(const Shape &s, int64_t T, const uint16_t *x, const float *Wr,
                                 const float *bias, float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *sa, int32_t *ap,
-                                const Plan &plan, int *arrivals, hipStream_t st)
+                                const Plan &plan, uint8_t *head, hipStream_t st)
 {
-    router_select_kernel<<<s.E, 1024, 0, st>>>((int)T, s.H, s.E, s.k, s.S, s.renorm, x, Wr, bias,
-                                               logits, ids, w, counts, offsets, sa, ap, plan, arrivals);
+    router_select_kernel<<<kPersistentGrid, 1024, 0, st>>>((int)T, s.H, s.E, s.k, s.S, s.renorm, x, Wr, bias,
+                                                           logits, ids, w, counts, offsets, sa, ap, plan, head);
     return hipGetLastError();
 }
 

@@ -114,7 +114,8 @@ def test_few_full_size(T, fmt):
 
 def test_few_shares_a_workspace_with_other_paths():
     """Small-batch launches between single-token launches and the four-launch path on one
-    workspace: every call correct, the launch counters count the persistent launches only."""
+    workspace: every call correct, the launch counters count the persistent launches (one
+    per call here: the four-launch path at T = 32 routes in one)."""
     ws = None
     n = 0
     for T in (8, 1, 16, 32, 3, 1, 8):
@@ -122,7 +123,7 @@ def test_few_shares_a_workspace_with_other_paths():
         c.upload()
         ws = c.workspace(32) if ws is None else ws
         g = _layer(c, ws)
-        n += 1 if T <= 16 else 0
+        n += 1
         assert _launches(ws) == n
         assert fm.workspace_status(ws) == 0
         w64 = check_routing(c, g, {})

@@ -482,9 +482,8 @@ def test_chain_batch_full(fmt):
 def test_graph_replays_match_eager(T):
     """The layer captured in a HIP graph (as the benchmark runs it), replayed several times
     with eager calls on the same workspace in between: every replay gives the eager
-    result bit for bit (the single-token launch's tags come from the launch counter in
-    device memory, so replays never reuse a tag; the small-batch arrival counter re-arms
-    itself; nothing is cleared with a memset node)."""
+    result bit for bit (the persistent launches' tags come from the launch counters in
+    device memory, so replays never reuse a tag; nothing is cleared with a memset node)."""
     c = Case(T, 256, 128, 256, 6, layer=2).upload()
     ws = c.workspace()
     y_eager = torch.zeros((T, 256), dtype=torch.int16, device="cuda")
