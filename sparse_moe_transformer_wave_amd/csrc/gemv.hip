@@ -14,9 +14,9 @@
 //   rounded to bf16.  The unit's token rows form the MFMA A operand; lanes whose row is
 //   past the unit's token count load nothing (most routed experts of a decode step hold
 //   one or two tokens).
-// Pass 2 (down): one workgroup per (work unit, 64 or fewer rows of H), outputs in fp32 to
-//   the workspace, one row per assignment (and per token for the shared expert).
-// Pass 3 (combine): y = o_shared + the k routed outputs in order, summed in fp32, to bf16.
+// Pass 2 (down): one workgroup per (work unit, 64 or fewer rows of H), per-slot outputs in
+//   fp32 to the workspace.
+// Pass 3 (combine): y = o_shared + the k routed slots in order, summed in fp32, to bf16.
 #include "common.h"
 
 #include <algorithm>
@@ -184,16 +184,13 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 // a batch in flight.  KS = 4 (few experts, e.g. a dense layer): one workgroup per (expert,
 // RW rows), wave w takes the w-th quarter of K and the quarters are summed through LDS, so
 // four times as many waves stream the same rows; RW = 8 (MFMA columns 8-15 repeat 0-7 and
-// are not stored) when 16-row workgroups would leave CUs without work.  The outputs go to
-// the workspace in fp32, indexed by assignment (o[t k + j][n]; the shared expert's token t
-// at row T k + t), so the combine finds them without the slot map.  Thousands of small
-// independent workgroups keep
+// are not stored) when 16-row workgroups would leave CUs without work.  Per-slot outputs
+// o[slot][n] go to the workspace in fp32.  Thousands of small independent workgroups keep
 // the weight stream busy the way the gate/up pass does.  I needs only be a multiple of 32:
 // a 4-bit super-chunk's lanes past I load nothing (zeros).
 template <int FMT, int KS, int RW = 16>
-__global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int dense_T, int TK, WSet w,
-                                                        const uint16_t *__restrict__ h,
-                                                        const int32_t *__restrict__ sa, Plan p,
+__global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int dense_T, WSet w,
+                                                        const uint16_t *__restrict__ h, Plan p,
                                                         float *__restrict__ o, uint16_t *__restrict__ y)
 {
     static_assert(KS == 1 || KS == 4, "K split over the 4 waves or none");
@@ -210,15 +207,6 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
     const int kw = KS == 1 ? 0 : wave;  // this wave's part of K
     const uint16_t *hr = h + (size_t)(base + min(r, cnt - 1)) * I;
     const bool has_tok = r < cnt;  // this lane's A row is one of the expert's tokens
-    // output rows of this lane's slots base + 4 g + i: the slot's assignment (routed) or the
-    // slot itself (shared expert, T k + t); -1 for none or an assignment out of range
-    int orow[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int ti = 4 * g + i;
-        const int a = dense_T || ti >= cnt ? -1 : e == E ? base + ti : sa[base + ti];
-        orow[i] = e == E || (a >= 0 && a < TK) ? a : -1;
-    }
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     float ts = 1.f;
     if (FMT == 0) {
@@ -309,17 +297,16 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
         if (ti < cnt && (KS == 1 || r < RW)) {
             if (dense_T)  // the combine of a dense layer is y = bf16(o): written here
                 y[(size_t)(base + ti) * H + row] = (uint16_t)f2bf(acc[i] * ts);
-            else if (orow[i] >= 0)
-                o[(size_t)orow[i] * H + row] = acc[i] * ts;
+            else
+                o[(size_t)(base + ti) * H + row] = acc[i] * ts;
         }
     }
 }
 
 // ------------------------------------------------------------------ pass 3: combine
-// y[t][n] = bf16(o[T*k + t][n] + sum_j w[t][j] * o[t*k + j][n]), summed in fp32 in that
-// order (shared first, then j ascending); 8 columns per thread.  Assignments whose slot
-// ap[t*k + j] is outside [0, T k) (dropped for an out-of-range expert id; the down pass
-// wrote no row for them) are skipped.
+// y[t][n] = bf16(o[T*k + t][n] + sum_j w[t][j] * o[ap[t*k + j]][n]), summed in fp32 in that
+// order (shared first, then j ascending); 8 columns per thread.  Slots outside [0, T k)
+// (assignments dropped for an out-of-range expert id) are skipped.
 __global__ __launch_bounds__(256) void gemv_combine_kernel(int T, int H, int k, int S,
                                                            const float *__restrict__ o,
                                                            const float *__restrict__ topk_w,
@@ -330,18 +317,12 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(int T, int H, int k, 
     const int gid = blockIdx.x * 256 + threadIdx.x;
     if (gid >= T * per_tok) return;
     const int t = gid / per_tok, c = (gid - t * per_tok) * 8;
-    // every load below is independent of the others: one round trip
     float wj[8];
     int sl[8];
-    f32x4 r0[8], r1[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         wj[j] = j < k ? topk_w[t * k + j] : 0.f;
         sl[j] = j < k ? ap[t * k + j] : -1;
-        if (j < k) {
-            r0[j] = *reinterpret_cast<const f32x4 *>(o + (size_t)(t * k + j) * H + c);
-            r1[j] = *reinterpret_cast<const f32x4 *>(o + (size_t)(t * k + j) * H + c + 4);
-        }
     }
     float acc[8];
     if (S) {
@@ -358,11 +339,13 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(int T, int H, int k, 
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        if (j < k && sl[j] >= 0 && sl[j] < T * k) {  // a dropped assignment (expert id out of range) has no slot
+        if (sl[j] >= 0 && sl[j] < T * k) {  // a dropped assignment (expert id out of range) has no slot
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(o + (size_t)sl[j] * H + c);
+            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(o + (size_t)sl[j] * H + c + 4);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                acc[i] += wj[j] * r0[j][i];
-                acc[4 + i] += wj[j] * r1[j][i];
+                acc[i] += wj[j] * a0[i];
+                acc[4 + i] += wj[j] * a1[i];
             }
         }
     }
@@ -395,15 +378,15 @@ static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, co
 // 16-row ones would still number fewer than the CUs.
 template <int FMT>
 static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, const uint16_t *h,
-                        const int32_t *sa, const Plan &plan, float *o, uint16_t *y, hipStream_t st)
+                        const Plan &plan, float *o, uint16_t *y, hipStream_t st)
 {
-    const int dense_T = s.E == 0 ? (int)T : 0, TK = (int)T * s.k;
+    const int dense_T = s.E == 0 ? (int)T : 0;
     if (FMT == 0 && maxU * (s.H / 64) >= 512)
-        gemv_down_kernel<FMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, TK, w, h, sa, plan, o, y);
+        gemv_down_kernel<FMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, w, h, plan, o, y);
     else if (maxU * (s.H / 16) >= 256)
-        gemv_down_kernel<FMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, TK, w, h, sa, plan, o, y);
+        gemv_down_kernel<FMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, w, h, plan, o, y);
     else
-        gemv_down_kernel<FMT, 4, 8><<<(unsigned)(maxU * (s.H / 8)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, TK, w, h, sa, plan, o, y);
+        gemv_down_kernel<FMT, 4, 8><<<(unsigned)(maxU * (s.H / 8)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, w, h, plan, o, y);
 }
 
 // With routed experts the plan lists units of at most 16 tokens (an expert with more is
@@ -420,7 +403,7 @@ static void launch_stream(const Shape &s, const WSet &w, int64_t T, const uint16
     const int maxU = (int)(std::min<int64_t>(T * s.k, s.E) + (T * s.k + kUnitRows - 1) / kUnitRows +
                            (int64_t)s.S * ((T + kUnitRows - 1) / kUnitRows));
     launch_gateup<FMT>(s, w, T, maxU, x, sa, plan, h, st);
-    launch_down<FMT>(s, w, T, maxU, h, sa, plan, o, y, st);
+    launch_down<FMT>(s, w, T, maxU, h, plan, o, y, st);
     if (s.E == 0) return;
     const int nthreads = (int)T * (s.H / 8);
     gemv_combine_kernel<<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>((int)T, s.H, s.k, s.S, o, topk_w, ap, y);
