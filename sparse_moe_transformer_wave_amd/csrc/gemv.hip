@@ -23,6 +23,14 @@
 
 namespace flint {
 
+// 4-bit gate/up: super-chunks of 128 columns a wave loads per step (two measured 3-6 %
+// slower per NVFP4 / INT4 layer at T = 8 and 32).
+constexpr int kGuSteps = 1;
+// 4-bit down with K split over the waves: 16-row groups per workgroup.  Two groups (half
+// as many workgroups, each with twice the codes in flight and one set of token fragments)
+// measured 4-5 % faster per NVFP4 layer at T = 8 and 32 than one; four measured in between.
+constexpr int kDnGroups = 2;
+
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 __device__ __forceinline__ const uint8_t *expert_base(const WMat &m, int e, int E, size_t bytes)
@@ -123,38 +131,47 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
         const uint8_t *SF0 = expert_sf(wm, e, E, (size_t)I * srow) + (size_t)(i0 + (r & 7)) * srow;
         xr = x + (size_t)tix * H;
         const int nsc = (H + 127) / 128;
-        for (int sc = wave; sc < nsc; sc += 4) {
-            const int kb = sc * 128 + g * 32;
-            const bool in = kb < H;  // false only in a last super-chunk of 64 columns (NVFP4)
-            u32x4 qv[RG], a[4];
-            uint32_t sb[RG];
+        // kGuSteps super-chunks of the wave (sc, sc + 4, ...) per step: all their loads in
+        // flight together, then their products in ascending K order
+        for (int sc0 = wave; sc0 < nsc; sc0 += 4 * kGuSteps) {
+            u32x4 qv[kGuSteps][RG], a[kGuSteps][4];
+            uint32_t sb[kGuSteps][RG];
 #pragma unroll
-            for (int q = 0; q < RG; q++) {
-                qv[q] = in ? ld16(Q0 + (size_t)q * 8 * (H / 2) + kb / 2) : u32x4{0u, 0u, 0u, 0u};
-                sb[q] = in ? *reinterpret_cast<const uint16_t *>(SF0 + (size_t)q * 8 * srow + (FMT == 1 ? kb / 16 : 2 * sc))
-                           : 0u;
+            for (int s = 0; s < kGuSteps; s++) {
+                const int sc = sc0 + 4 * s, kb = sc * 128 + g * 32;
+                const bool in = sc < nsc && kb < H;  // kb >= H only in a last super-chunk of 64 columns (NVFP4)
+#pragma unroll
+                for (int q = 0; q < RG; q++) {
+                    qv[s][q] = in ? ld16(Q0 + (size_t)q * 8 * (H / 2) + kb / 2) : u32x4{0u, 0u, 0u, 0u};
+                    sb[s][q] = in ? *reinterpret_cast<const uint16_t *>(SF0 + (size_t)q * 8 * srow + (FMT == 1 ? kb / 16 : 2 * sc))
+                                  : 0u;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) a[s][j] = has_tok && in ? ld16(xr + kb + 8 * j) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++) a[j] = has_tok && in ? ld16(xr + kb + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+            for (int s = 0; s < kGuSteps; s++) {
+                if (sc0 + 4 * s >= nsc) break;
 #pragma unroll
-            for (int q = 0; q < RG; q++) {
-                if (FMT == 1) {
+                for (int q = 0; q < RG; q++) {
+                    if (FMT == 1) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const bf16x8 bv = as_bf16x8(dequant8_stream(qv[q][j], e4m3_to_f32((sb[q] >> (8 * (j >> 1))) & 0xffu)));
-                        acc[q] = mfma16x16x32(as_bf16x8(a[j]), bv, acc[q]);
+                        for (int j = 0; j < 4; j++) {
+                            const bf16x8 bv = as_bf16x8(dequant8_stream(qv[s][q][j], e4m3_to_f32((sb[s][q] >> (8 * (j >> 1))) & 0xffu)));
+                            acc[q] = mfma16x16x32(as_bf16x8(a[s][j]), bv, acc[q]);
+                        }
+                    } else {
+                        // INT4: the super-chunk is one scale group and its 4 MFMAs contract
+                        // inside it, so they run on the exact integer codes and the group
+                        // scale of the lane's column (its own row) multiplies their fp32 sum.
+                        f32x4 gsum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            gsum = mfma16x16x32(as_bf16x8(a[s][j]), as_bf16x8(int4_bf16x8(qv[s][q][j])), gsum);
+                        const float sv = bf2f(sb[s][q]);
+                        acc[q] = f32x4{acc[q][0] + gsum[0] * sv, acc[q][1] + gsum[1] * sv,
+                                       acc[q][2] + gsum[2] * sv, acc[q][3] + gsum[3] * sv};
                     }
-                } else {
-                    // INT4: the super-chunk is one scale group and its 4 MFMAs contract
-                    // inside it, so they run on the exact integer codes and the group scale
-                    // of the lane's column (its own row) multiplies their fp32 sum.
-                    f32x4 gsum = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        gsum = mfma16x16x32(as_bf16x8(a[j]), as_bf16x8(int4_bf16x8(qv[q][j])), gsum);
-                    const float sv = bf2f(sb[q]);
-                    acc[q] = f32x4{acc[q][0] + gsum[0] * sv, acc[q][1] + gsum[1] * sv,
-                                   acc[q][2] + gsum[2] * sv, acc[q][3] + gsum[3] * sv};
                 }
             }
         }
@@ -184,30 +201,36 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(int T, int H, int I, i
 // a batch in flight.  KS = 4 (few experts, e.g. a dense layer): one workgroup per (expert,
 // RW rows), wave w takes the w-th quarter of K and the quarters are summed through LDS, so
 // four times as many waves stream the same rows; RW = 8 (MFMA columns 8-15 repeat 0-7 and
-// are not stored) when 16-row workgroups would leave CUs without work.  Per-slot outputs
+// are not stored) when 16-row workgroups would leave CUs without work; DG > 1 (4-bit
+// weights): DG groups of RW rows per workgroup, their codes loaded together against the
+// same token fragments.  Per-slot outputs
 // o[slot][n] go to the workspace in fp32.  Thousands of small independent workgroups keep
 // the weight stream busy the way the gate/up pass does.  I needs only be a multiple of 32:
 // a 4-bit super-chunk's lanes past I load nothing (zeros).
-template <int FMT, int KS, int RW = 16>
+template <int FMT, int KS, int RW = 16, int DG = 1>
 __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int dense_T, WSet w,
                                                         const uint16_t *__restrict__ h, Plan p,
                                                         float *__restrict__ o, uint16_t *__restrict__ y)
 {
     static_assert(KS == 1 || KS == 4, "K split over the 4 waves or none");
     static_assert(RW == 16 || RW == 8, "16 or 8 rows per workgroup");
-    __shared__ f32x4 red[KS == 4 ? 3 : 1][64];
-    const int nrb = KS == 1 ? H / 64 : H / RW;
+    static_assert(DG == 1 || (FMT != 0 && KS == 4), "row groups only for split-K 4-bit workgroups");
+    __shared__ f32x4 red[KS == 4 ? 3 : 1][DG][64];
+    const int nrb = KS == 1 ? H / 64 : H / (RW * DG);
     const int u = blockIdx.x / nrb, nb = blockIdx.x - u * nrb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     // dense_T > 0: a dense layer of dense_T tokens, unit u = tokens 16 u .. 16 u + 15, outputs y
     const int nT = dense_T ? (dense_T + 15) / 16 : p.meta[0];
     const int e = dense_T ? E : p.touched[u], base = dense_T ? 16 * u : p.tbase[u], cnt = dense_T ? min(16, dense_T - 16 * u) : p.tcount[u];
     if (u >= nT) return;
-    const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * RW + (r % RW);  // MFMA column r of this wave
+    // MFMA column r of this wave in row group 0 (group q: + q RW)
+    const int row = KS == 1 ? nb * 64 + wave * 16 + r : nb * RW * DG + (r % RW);
     const int kw = KS == 1 ? 0 : wave;  // this wave's part of K
     const uint16_t *hr = h + (size_t)(base + min(r, cnt - 1)) * I;
     const bool has_tok = r < cnt;  // this lane's A row is one of the expert's tokens
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[DG];
+#pragma unroll
+    for (int q = 0; q < DG; q++) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ts = 1.f;
     if (FMT == 0) {
         const uint16_t *Wd = reinterpret_cast<const uint16_t *>(expert_base(w.down, e, E, (size_t)H * I * 2)) +
@@ -225,7 +248,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
 #pragma unroll
             for (int i = 0; i < NB; i++) a[i] = has_tok ? ld16(hg + (c0 + i) * 32) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < NB; i++) acc = mfma16x16x32(as_bf16x8(a[i]), as_bf16x8(b[i]), acc);
+            for (int i = 0; i < NB; i++) acc[0] = mfma16x16x32(as_bf16x8(a[i]), as_bf16x8(b[i]), acc[0]);
         }
         if (c0 < ce) {                         // the last, partial batch: its loads in flight together
             u32x4 b[NB], a[NB];
@@ -236,7 +259,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
                 a[i] = c0 + i < ce && has_tok ? ld16(hg + (c0 + i) * 32) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < NB; i++)
-                if (c0 + i < ce) acc = mfma16x16x32(as_bf16x8(a[i]), as_bf16x8(b[i]), acc);
+                if (c0 + i < ce) acc[0] = mfma16x16x32(as_bf16x8(a[i]), as_bf16x8(b[i]), acc[0]);
         }
     } else {
         const size_t srow = scale_row_bytes(FMT, I);
@@ -247,60 +270,73 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(int H, int I, int E, int
         // split-K workgroups take one super-chunk per step (two measured 0.4-2.4 % slower)
         constexpr int NB = KS == 1 ? 6 : 1;
         for (int s0 = nsc * kw / KS; s0 < se; s0 += NB) {
-            u32x4 q[NB], a[NB][4];
-            uint32_t sb[NB];
+            u32x4 q[NB][DG], a[NB][4];
+            uint32_t sb[NB][DG];
 #pragma unroll
             for (int i = 0; i < NB; i++) {
                 const int kb = (s0 + i) * 128 + g * 32;
                 const bool in = s0 + i < se && kb < I;  // kb >= I only in a partial last super-chunk
-                q[i] = in ? ld16(Qd + kb / 2) : u32x4{0u, 0u, 0u, 0u};
-                sb[i] = in ? *reinterpret_cast<const uint16_t *>(Sd + (FMT == 1 ? kb / 16 : 2 * (s0 + i))) : 0u;
+#pragma unroll
+                for (int d = 0; d < DG; d++) {
+                    q[i][d] = in ? ld16(Qd + (size_t)d * RW * (I / 2) + kb / 2) : u32x4{0u, 0u, 0u, 0u};
+                    sb[i][d] = in ? *reinterpret_cast<const uint16_t *>(Sd + (size_t)d * RW * srow + (FMT == 1 ? kb / 16 : 2 * (s0 + i)))
+                                  : 0u;
+                }
 #pragma unroll
                 for (int j = 0; j < 4; j++) a[i][j] = in && has_tok ? ld16(hr + kb + 8 * j) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int i = 0; i < NB; i++) {
                 if (s0 + i < se) {
-                    if (FMT == 1) {
 #pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            const bf16x8 bv = as_bf16x8(dequant8_stream(q[i][j], e4m3_to_f32((sb[i] >> (8 * (j >> 1))) & 0xffu)));
-                            acc = mfma16x16x32(as_bf16x8(a[i][j]), bv, acc);
+                    for (int d = 0; d < DG; d++) {
+                        if (FMT == 1) {
+#pragma unroll
+                            for (int j = 0; j < 4; j++) {
+                                const bf16x8 bv = as_bf16x8(dequant8_stream(q[i][d][j], e4m3_to_f32((sb[i][d] >> (8 * (j >> 1))) & 0xffu)));
+                                acc[d] = mfma16x16x32(as_bf16x8(a[i][j]), bv, acc[d]);
+                            }
+                        } else {  // INT4: integer codes per scale group, then the row's group scale
+                            f32x4 gsum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int j = 0; j < 4; j++)
+                                gsum = mfma16x16x32(as_bf16x8(a[i][j]), as_bf16x8(int4_bf16x8(q[i][d][j])), gsum);
+                            const float sv = bf2f(sb[i][d]);
+                            acc[d] = f32x4{acc[d][0] + gsum[0] * sv, acc[d][1] + gsum[1] * sv, acc[d][2] + gsum[2] * sv,
+                                           acc[d][3] + gsum[3] * sv};
                         }
-                    } else {  // INT4: integer codes per scale group, then the row's group scale
-                        f32x4 gsum = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            gsum = mfma16x16x32(as_bf16x8(a[i][j]), as_bf16x8(int4_bf16x8(q[i][j])), gsum);
-                        const float sv = bf2f(sb[i]);
-                        acc = f32x4{acc[0] + gsum[0] * sv, acc[1] + gsum[1] * sv, acc[2] + gsum[2] * sv,
-                                    acc[3] + gsum[3] * sv};
                     }
                 }
             }
         }
     }
     if (KS == 4) {  // waves 1..3 hand their partial sums to wave 0 (K order: wave 0 first)
-        if (wave > 0) red[KS == 4 ? wave - 1 : 0][lane] = acc;
+#pragma unroll
+        for (int d = 0; d < DG; d++)
+            if (wave > 0) red[KS == 4 ? wave - 1 : 0][d][lane] = acc[d];
         __syncthreads();
         if (wave > 0) return;
 #pragma unroll
-        for (int q = 0; q < 3; q++) {
-            const f32x4 v = red[KS == 4 ? q : 0][lane];
-            acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
-        }
+        for (int d = 0; d < DG; d++)
+#pragma unroll
+            for (int q = 0; q < 3; q++) {
+                const f32x4 v = red[KS == 4 ? q : 0][d][lane];
+                acc[d] = f32x4{acc[d][0] + v[0], acc[d][1] + v[1], acc[d][2] + v[2], acc[d][3] + v[3]};
+            }
     }
     // D[m][n]: lane 16 (m / 4) + n, element m % 4; rows (slots) of this lane: m = 4 g + i.
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int ti = 4 * g + i;
-        if (ti < cnt && (KS == 1 || r < RW)) {
-            if (dense_T)  // the combine of a dense layer is y = bf16(o): written here
-                y[(size_t)(base + ti) * H + row] = (uint16_t)f2bf(acc[i] * ts);
-            else
-                o[(size_t)(base + ti) * H + row] = acc[i] * ts;
+    for (int d = 0; d < DG; d++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int ti = 4 * g + i;
+            if (ti < cnt && (KS == 1 || r < RW)) {
+                if (dense_T)  // the combine of a dense layer is y = bf16(o): written here
+                    y[(size_t)(base + ti) * H + row + d * RW] = (uint16_t)f2bf(acc[d][i] * ts);
+                else
+                    o[(size_t)(base + ti) * H + row + d * RW] = acc[d][i] * ts;
+            }
         }
-    }
 }
 
 // ------------------------------------------------------------------ pass 3: combine
@@ -374,8 +410,9 @@ static void launch_gateup(const Shape &s, const WSet &w, int64_t T, int maxU, co
 
 // Split K over the waves when 64-row workgroups would leave most CUs idle, and always for
 // 4-bit weights (their short rows make a 64-row workgroup mostly wait: 16-row workgroups
-// measured 2-3 % faster per NVFP4 layer at T = 8 and 32), and take 8 rows per workgroup when
-// 16-row ones would still number fewer than the CUs.
+// measured 2-3 % faster per NVFP4 layer at T = 8 and 32; kDnGroups of them per workgroup
+// when that still leaves a workgroup per CU), and take 8 rows per workgroup when 16-row ones
+// would still number fewer than the CUs.
 template <int FMT>
 static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, const uint16_t *h,
                         const Plan &plan, float *o, uint16_t *y, hipStream_t st)
@@ -383,6 +420,9 @@ static void launch_down(const Shape &s, const WSet &w, int64_t T, int maxU, cons
     const int dense_T = s.E == 0 ? (int)T : 0;
     if (FMT == 0 && maxU * (s.H / 64) >= 512)
         gemv_down_kernel<FMT, 1><<<(unsigned)(maxU * (s.H / 64)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, w, h, plan, o, y);
+    else if (FMT != 0 && kDnGroups > 1 && s.H % (16 * kDnGroups) == 0 && maxU * (s.H / (16 * kDnGroups)) >= 256)
+        gemv_down_kernel<FMT, 4, 16, (FMT != 0 ? kDnGroups : 1)><<<(unsigned)(maxU * (s.H / (16 * kDnGroups))), 256, 0, st>>>(
+            s.H, s.I, s.E, dense_T, w, h, plan, o, y);
     else if (maxU * (s.H / 16) >= 256)
         gemv_down_kernel<FMT, 4><<<(unsigned)(maxU * (s.H / 16)), 256, 0, st>>>(s.H, s.I, s.E, dense_T, w, h, plan, o, y);
     else
