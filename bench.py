@@ -110,6 +110,21 @@ def expert_bytes(fmt, H_, I_):
     return 3 * (I_ * H_ // 2 + I_ * H_ // 64)
 
 
+def algorithmic_bytes(fmt, shp, T, touched):
+    """HBM bytes one layer call must move: the weights of the `touched` routed experts and of
+    the shared expert once each, the fp32 router matrix, the bf16 tokens read and the bf16
+    outputs written."""
+    H_, I_, E_, _, S_ = shp
+    return (touched + S_) * expert_bytes(fmt, H_, I_) + E_ * H_ * 4 + 2 * T * H_ * 2
+
+
+def layer_flops(shp, T):
+    """Multiply-add flops of one layer call's expert FFNs: k routed + S shared experts per
+    token, three H x I products each (gate, up, down)."""
+    H_, I_, _, k_, S_ = shp
+    return 2.0 * T * (k_ + S_) * 3 * H_ * I_
+
+
 # ------------------------------------------------------------------ counter traffic
 def csrc_digest():
     """sha256 over the HIP sources: counter-derived traffic is reported only while the
@@ -368,9 +383,8 @@ def run_config(name, args, torch, fm, dg, pools):
         touched = [len(set(r.reshape(-1).tolist())) for r in ids.cpu().numpy()]
     else:
         touched = [TOPK if E_ else 0] * L  # a single token touches exactly k routed experts
-    xb = expert_bytes(fmt, H_, I_)
-    alg_bytes = [(u + S_) * xb + E_ * H_ * 4 + 4 * T * H_ for u in touched]
-    flops_layer = 2.0 * T * (k_ + S_) * 3 * H_ * I_
+    alg_bytes = [algorithmic_bytes(fmt, shp, T, u) for u in touched]
+    flops_layer = layer_flops(shp, T)
 
     def capture(n_steps):
         g = torch.cuda.CUDAGraph()
