@@ -62,3 +62,51 @@ def test_bf16_rounding_and_determinism():
 def test_rank_permutation_is_a_permutation():
     r = dg.rank_permutation(256, 0, dg.stream_id(0, dg.KIND_ZIPF, 0))
     assert sorted(r) == list(range(1, 257))
+
+
+def _digest_script():
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_input_digests.py")
+    spec = importlib.util.spec_from_file_location("make_input_digests", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_parity_inputs_match_recorded_digests():
+    """The parity tests' seeded inputs (tiny and full-size tokens, router weights, Zipf bias,
+    experts in bf16 and as the reference quantisers' NVFP4 / INT4 codes) are the bytes whose
+    SHA-256 digests tests/golden/input_digests.json records."""
+    import json
+    mod = _digest_script()
+    rec = json.load(open(mod.OUT))
+    assert rec["seed"] == 0 and rec["zipf_c"] == dg.ZIPF_C
+    now = mod.compute()
+    assert sorted(now) == sorted(rec["tensors"])
+    bad = [k for k in now if now[k] != rec["tensors"][k]]
+    assert not bad, bad
+
+
+def test_recorded_digests_describe_the_parity_cases():
+    """The tiny parity case builds its inputs from the same draws the digests cover."""
+    import hashlib
+    import json
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from moe_cases import Case
+    import sparse_moe_transformer_wave_amd as fm
+    rec = json.load(open(_digest_script().OUT))["tensors"]
+    sha = lambda a: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+    c = Case(32, 256, 128, 256, 6)
+    assert sha(c.x) == rec["tiny/x"]["sha256"]
+    assert sha(c.Wr) == rec["tiny/Wr"]["sha256"]
+    for name in ("gate", "up", "down"):
+        both = np.concatenate([c.host[name], c.host_sh[name]])
+        assert sha(both) == rec["tiny/bf16/all_experts/" + name]["sha256"]
+    c4 = Case(32, 256, 128, 256, 6, fmt=fm.WFMT_INT4, experts=[0, 255])
+    for name in ("q_gate", "sb_down"):
+        assert sha(c4.host[name][0]) == rec["tiny/int4/expert0/" + name]["sha256"]
+        assert sha(c4.host[name][255]) == rec["tiny/int4/expert255/" + name]["sha256"]
+        assert sha(c4.host_sh[name][0]) == rec["tiny/int4/expert256/" + name]["sha256"]
